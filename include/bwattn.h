@@ -1,0 +1,124 @@
+/*
+ * bwattn.h - blockwise exact causal attention with RoPE and a packing mask,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the attention core of the Large World Model training
+ * stack (arXiv 2402.08268, "World Model on Million-Length Video And Language
+ * With Blockwise RingAttention"):
+ *   - exact softmax attention computed blockwise (query blocks stream K/V
+ *     blocks and merge partial results with an online-softmax running max and
+ *     sum), as in the ring/blockwise attention fused with FlashAttention that
+ *     the paper trains with (zhao9797 page "LWM (Large World Model)", section
+ *     模型架构; elamur.ai summary page, Summary: no approximation);
+ *   - causal masking of a decoder-only autoregressive model (zhao9797 page,
+ *     模型架构);
+ *   - the masked-sequence-packing mask: tokens of one packed example attend
+ *     only to tokens of the same example (zhao9797 page, 训练方法, "Masked
+ *     Sequence Packing");
+ *   - standard RoPE with a context-scaled base theta, 1e6 at 32K up to 5e7 at
+ *     1M (zhao9797 page, 模型架构 and the Stage I table of 训练方法).
+ * The cross-device K/V ring of the paper becomes an in-HBM loop over K/V
+ * blocks on one GPU (kv_chunk below gives the ring's visiting order).
+ *
+ * Conventions for every entry point
+ *   - Tensors are device pointers.  q, k, v, o, dO, dq, dk, dv are bf16
+ *     [B,H,S,D] contiguous (D innermost).  segment_ids and positions are int32
+ *     [B,S].  lse is fp32 [B,H,S].  All pointers must be 16-byte aligned.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream).  The library never allocates, frees or synchronizes, and keeps
+ *     no pointer after returning.  The caller owns every buffer, including the
+ *     workspace sized by attn_workspace_bytes, and keeps them alive until the
+ *     stream work has finished.  Entry points keep no state and are
+ *     thread-safe.
+ *   - Every argument is checked before any HIP call.  The return value is an
+ *     attn_status; no exception crosses the ABI and the library never aborts.
+ *     Device-side values (segment ids, positions) are not checked: any int32
+ *     values are legal.  Faults inside kernels surface at the next stream
+ *     synchronisation, as for any HIP kernel.
+ *
+ * Reading of the pages where they are silent (softmax scale, RoPE pairing,
+ * positions under packing) is stated at each field.
+ */
+#ifndef BWATTN_H
+#define BWATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1, /* null required pointer, bad size, misalignment, overflow, struct_size */
+  ATTN_ERR_UNSUPPORTED = 2, /* head_dim not compiled, or the device is not gfx950 */
+  ATTN_ERR_WORKSPACE = 3,   /* workspace pointer null or smaller than attn_workspace_bytes */
+  ATTN_ERR_HIP = 4          /* a HIP launch or query failed */
+} attn_status;
+
+typedef struct {
+  int32_t struct_size;   /* must equal sizeof(attn_params): guards against ABI drift          */
+  int32_t batch;         /* B >= 1                                                           */
+  int32_t heads;         /* H >= 1                                                           */
+  int32_t seqlen;        /* S >= 1                                                           */
+  int32_t head_dim;      /* D, 64 or 128                                                     */
+  float softmax_scale;   /* <= 0 selects 1/sqrt(D) (the pages give no scale)                 */
+  int32_t causal;        /* 1: key j visible to query i only if j <= i (sequence index)      */
+                         /* 0: no causal term (the packing mask still applies)               */
+  double rope_theta;     /* RoPE base; <= 0 disables RoPE (q, k used as given).  Pairs       */
+                         /* (x[2i], x[2i+1]) rotate by pos * theta^(-2i/D), angle in fp64.   */
+  int32_t kv_chunk;      /* 0: K/V blocks visited in natural order.  > 0: ring order: the    */
+                         /* sequence is cut in chunks of kv_chunk keys (a multiple of 64);   */
+                         /* queries of chunk r visit chunk r, r-1, ..., 0, C-1, ..., r+1.    */
+  int32_t deterministic; /* reserved, must be 0 or 1; 1 asks attn_bwd for a bitwise          */
+                         /* reproducible result (no float atomics)                           */
+} attn_params;
+
+/* Name of a status code (static string). */
+const char* attn_status_string(int status);
+
+/* Message of the last error returned on the calling thread ("" if none). */
+const char* attn_last_error(void);
+
+/* Bytes of device workspace that attn_fwd (which = 0) or attn_bwd (which = 1)
+ * needs for these parameters; 0 if the parameters are invalid.  rope_apply
+ * needs none. */
+size_t attn_workspace_bytes(const attn_params* p, int32_t which);
+
+/* RoPE on x (bf16 [B,H,S,D]) into y (same shape; y may equal x): each pair
+ * (x[2i], x[2i+1]) of a row at position pos rotates by a = pos * theta^(-2i/D)
+ * (inverse != 0: by -a, the transpose of the rotation).  positions NULL means
+ * pos = s.  The angle is formed and reduced in fp64; the rotation is done in
+ * fp32 and rounded to bf16 (round to nearest even).  Uses p->batch, heads,
+ * seqlen, head_dim and rope_theta (which must be > 0).  RoPE as "standard
+ * RoPE" with scaled theta: zhao9797 page, 模型架构. */
+int rope_apply(const attn_params* p, const void* x, void* y, const int32_t* positions, int32_t inverse,
+               void* stream);
+
+/* Forward: o = softmax(scale * q' k'^T + mask) v and lse (natural log) per
+ * query row, where q' and k' are q and k after RoPE at `positions`, and the
+ * mask allows key j for query i iff segment_ids[j] == segment_ids[i] and
+ * (if causal) j <= i.  q and k are passed un-rotated.  segment_ids NULL: one
+ * segment per batch row; positions NULL: pos = s.  Exact attention computed
+ * blockwise with an online softmax (zhao9797 page, 模型架构; packing mask:
+ * 训练方法).  o: bf16 [B,H,S,D]; lse: fp32 [B,H,S], kept for attn_bwd.
+ * workspace: attn_workspace_bytes(p, 0) bytes of device memory. */
+int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, const int32_t* segment_ids,
+             const int32_t* positions, void* o, float* lse, void* workspace, size_t workspace_bytes,
+             void* stream);
+
+/* Backward of attn_fwd: given o and lse from attn_fwd on the same inputs and
+ * the output gradient d_o, writes dq, dk, dv (bf16 [B,H,S,D]), the gradients
+ * with respect to the un-rotated q and k and to v (the RoPE backward is
+ * included).  The attention probabilities are recomputed from lse, so memory
+ * stays linear in S.  workspace: attn_workspace_bytes(p, 1) bytes. */
+int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v, const void* o,
+             const float* lse, const void* d_o, const int32_t* segment_ids, const int32_t* positions,
+             void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BWATTN_H */

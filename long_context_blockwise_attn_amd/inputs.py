@@ -1,0 +1,176 @@
+"""Seeded synthetic inputs shaped like the workloads on the pages.
+
+This module holds no attention arithmetic: it only draws random tensors and
+the packing structure (segment ids and per-document positions).  Both the GPU
+path and the oracle take their inputs from here, so the tests and the
+benchmark see the same values on both sides.
+
+Workloads (B batch, H heads, D head dim, S sequence length):
+
+tiny
+    B1 H2 D64 S1024, q/k/v float32 N(0,1) from numpy PCG64(seed), cast to
+    bf16 (round to nearest even) for the GPU; theta 1e4; one document; causal.
+llama7b_32k
+    B1 H32 D128 S32768 (a LLaMA-2-7B attention layer; zhao9797 page, 模型架构),
+    bf16 N(0,1); theta 1e6 (the 32K stage, 训练方法 Stage I table); one
+    document; causal.
+packing_128k
+    B1 H32 D128 S131072, theta 1e7 (the 128K stage); documents with lengths
+    log-uniform in [512, 32768] packed into one row (masked sequence packing,
+    训练方法), positions restart per document; causal + segment mask.
+video_text_256k
+    B1 H32 D128 S262144, theta 1e7; records of a text span (uniform 64..2048
+    tokens) and a 30-frame clip of 256 vision tokens per frame (数据: video
+    sampled at 30 frames; 模型架构: 256 tokens per 256x256 frame, <eof> after
+    every frame but the last, <eov> after the last, <vision>...</vision>
+    around the clip), one record per segment, order of text and clip drawn at
+    random (数据: modality order swapped at random); causal + segment mask.
+full_1m
+    B1 H32 D128 S1048576, theta 5e7 (the 1M stage); one document; causal; the
+    sequence is cut into 64 chunks of 16384 and K/V are visited in ring order.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+# tokens of one 30-frame clip: 30 frames x 256 tokens, 29 <eof>, 1 <eov>,
+# <vision> and </vision>
+FRAMES_PER_CLIP = 30
+TOKENS_PER_FRAME = 256
+CLIP_TOKENS = FRAMES_PER_CLIP * TOKENS_PER_FRAME + (FRAMES_PER_CLIP - 1) + 1 + 2
+
+
+@dataclass
+class Workload:
+    name: str
+    batch: int
+    heads: int
+    head_dim: int
+    seqlen: int
+    theta: float
+    causal: bool = True
+    packing: str = "none"  # none | loguniform | video_text
+    kv_chunk: int = 0
+    backward: bool = True
+    seed: int = 0
+    input_dtype: str = "bf16"  # bf16, or fp32 drawn then rounded to bf16
+    notes: str = ""
+    extra: dict = field(default_factory=dict)
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, 2, 64, 1024, 1e4, backward=False, seed=1, input_dtype="fp32"),
+    "llama7b_32k": Workload("llama7b_32k", 1, 32, 128, 32768, 1e6, seed=2),
+    "packing_128k": Workload("packing_128k", 1, 32, 128, 131072, 1e7, packing="loguniform", seed=3),
+    "video_text_256k": Workload("video_text_256k", 1, 32, 128, 262144, 1e7, packing="video_text",
+                                backward=False, seed=4),
+    "full_1m": Workload("full_1m", 1, 32, 128, 1048576, 5e7, kv_chunk=16384, seed=5),
+}
+
+
+def loguniform_lengths(total: int, lo: int, hi: int, seed: int) -> list[int]:
+    """Document lengths L = round(exp(U(ln lo, ln hi))) drawn until they cover
+    `total` tokens; the last one is cut so the lengths sum to `total`."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out, acc = [], 0
+    while acc < total:
+        L = int(round(math.exp(rng.uniform(math.log(lo), math.log(hi)))))
+        L = min(L, total - acc)
+        out.append(L)
+        acc += L
+    return out
+
+
+def video_text_lengths(total: int, seed: int) -> list[int]:
+    """Record lengths: a text span of U{64..2048} tokens plus one clip of
+    CLIP_TOKENS tokens; one record per segment, last record cut to fit.  The
+    text-first or clip-first order is drawn too but does not change a record's
+    length, so only the length is returned."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out, acc = [], 0
+    while acc < total:
+        text = int(rng.integers(64, 2049))
+        _text_first = bool(rng.integers(0, 2))
+        L = min(text + CLIP_TOKENS, total - acc)
+        out.append(L)
+        acc += L
+    return out
+
+
+def segments_from_lengths(lengths, batch: int = 1):
+    """int32 [B,S] segment ids (document index) and positions restarting at 0
+    in every document; the same packing for every batch row."""
+    seg = np.concatenate([np.full(L, i, dtype=np.int32) for i, L in enumerate(lengths)])
+    pos = np.concatenate([np.arange(L, dtype=np.int32) for L in lengths])
+    return np.tile(seg, (batch, 1)), np.tile(pos, (batch, 1))
+
+
+def packing(w: Workload):
+    """(segment_ids, positions, lengths) as int32 numpy [B,S]; segment_ids is
+    None for a single document (positions are then 0..S-1)."""
+    S = w.seqlen
+    if w.packing == "none":
+        return None, np.tile(np.arange(S, dtype=np.int32), (w.batch, 1)), [S]
+    if w.packing == "loguniform":
+        lengths = loguniform_lengths(S, 512, 32768, w.seed)
+    elif w.packing == "video_text":
+        lengths = video_text_lengths(S, w.seed)
+    else:
+        raise ValueError(w.packing)
+    seg, pos = segments_from_lengths(lengths, w.batch)
+    return seg, pos, lengths
+
+
+def randn_bf16(shape, seed: int, device="cpu", fp32_numpy: bool = False):
+    """bf16 N(0,1) tensor.  fp32_numpy=True draws float32 with numpy PCG64 and
+    rounds to bf16 (round to nearest even, torch's cast); otherwise torch's
+    generator on `device` draws it."""
+    import torch
+
+    if fp32_numpy:
+        rng = np.random.Generator(np.random.PCG64(seed))
+        x = torch.from_numpy(rng.standard_normal(size=shape, dtype=np.float32))
+        return x.to(torch.bfloat16).to(device)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+
+
+def make_qkv(w: Workload, device="cpu", with_grad_out: bool = False, heads: int | None = None):
+    """q, k, v (and dO) bf16 [B,H,S,D] for workload w.  heads overrides H
+    (a subset of a workload's heads for cheaper tests)."""
+    H = w.heads if heads is None else heads
+    shape = (w.batch, H, w.seqlen, w.head_dim)
+    fp32 = w.input_dtype == "fp32"
+    if fp32:
+        # one numpy draw for q, k, v in sequence so the seed fixes all three
+        rng = np.random.Generator(np.random.PCG64(w.seed))
+        import torch
+
+        ts = [torch.from_numpy(rng.standard_normal(size=shape, dtype=np.float32)).to(torch.bfloat16).to(device)
+              for _ in range(4 if with_grad_out else 3)]
+    else:
+        ts = [randn_bf16(shape, w.seed * 16 + i, device) for i in range(4 if with_grad_out else 3)]
+    return tuple(ts)
+
+
+def random_case(B, H, S, D, seed, n_docs=0, device="cpu"):
+    """Small random case for parity tests: bf16 q, k, v, dO and, if n_docs > 0,
+    n_docs contiguous documents of random lengths (positions restart per
+    document); otherwise one document with positions 0..S-1."""
+    import torch
+
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if n_docs > 0:
+        cuts = np.sort(rng.choice(np.arange(1, S), size=min(n_docs - 1, S - 1), replace=False))
+        lengths = np.diff(np.concatenate([[0], cuts, [S]])).astype(int).tolist()
+        seg, pos = segments_from_lengths(lengths, B)
+    else:
+        seg, pos = None, np.tile(np.arange(S, dtype=np.int32), (B, 1))
+    shape = (B, H, S, D)
+    ts = [torch.from_numpy(rng.standard_normal(size=shape, dtype=np.float32)).to(torch.bfloat16).to(device)
+          for _ in range(4)]
+    return ts, seg, pos
