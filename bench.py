@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Benchmark of blockwise exact causal attention, forward + backward, on one
+MI355X.
+
+One step is one pass of the whole path over one batch: attn_fwd (RoPE of q and
+k, tile schedule, forward kernel) then attn_bwd (RoPE, tile schedule, dQ and
+Delta kernel, dK/dV kernel with the RoPE backward).  Inputs are synthetic and
+already resident in HBM when the timed region starts.
+
+Throughput counts algorithmic FLOPs only: 4*D per visible (query, key) pair
+for the forward and 10*D for the backward (QK^T recomputed, dP, dV, dK, dQ),
+summed over heads; masked pairs are not credited.
+
+Prints one JSON line.  --gpus N with N > 1 exits: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "causal attention TFLOP/s fwd+bwd (32h×d128, S=32K–1M) and % of bf16 peak"
+# MI355X dense bf16 MFMA peak: 256 CUs x 4 SIMDs x 1024 FLOP/clk x 2.4 GHz (the 2.5 PFLOP/s figure)
+BF16_PEAK_TFLOPS = 2516.6
+HBM_PEAK_GBS = 8000.0
+KERNELS = {"rope": 0, "fwd": 1, "bwd_dq": 2, "bwd_dkdv": 3}
+
+
+def visible_pairs(lengths, causal=True):
+    """Number of visible (query, key) pairs of one batch row."""
+    L = np.asarray(lengths, dtype=np.int64)
+    return int(np.sum(L * (L + 1) // 2)) if causal else int(np.sum(L * L))
+
+
+def row_visible_counts(lengths):
+    return np.concatenate([np.arange(1, L + 1, dtype=np.int64) for L in lengths])
+
+
+def cpu_baseline(w, q, k, v, do, seg, pos, budget_s):
+    """Time the oracle (as it stands) on a sample of query rows of head 0:
+    forward and backward contributions of those rows.  Returns the dict for
+    the JSON line, in TFLOP/s with the same FLOP accounting as the GPU."""
+    import oracle
+
+    oracle.build(force=False)
+    S, D = w.seqlen, w.head_dim
+    lengths = w.extra["lengths"]
+    counts = row_visible_counts(lengths)
+    q0, k0, v0, d0 = (t[:1, :1].float().cpu().numpy().astype(np.float64) for t in (q, k, v, do))
+    seg0 = None if seg is None else seg[:1]
+    pos0 = pos[:1]
+
+    def run(n_rows):
+        rows = np.unique(np.linspace(0, S - 1, n_rows).astype(np.int64))
+        t0 = time.perf_counter()
+        oracle.attn_fwd(q0, k0, v0, seg0, pos0, theta=w.theta, causal=w.causal, rows=rows)
+        oracle.attn_bwd(q0, k0, v0, d0, seg0, pos0, theta=w.theta, causal=w.causal, rows=rows)
+        dt = time.perf_counter() - t0
+        flops = 14.0 * D * float(np.sum(counts[rows]))
+        return rows, dt, flops
+
+    rows, dt, flops = run(16)
+    n = int(min(S, max(16, 16 * budget_s / max(dt, 1e-3) * 0.8)))
+    rows, dt, flops = run(n)
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": "fwd+bwd of %d evenly spaced query rows of head 0 (of %d rows x %d heads), %.1f s; "
+                  "credited 14*D FLOPs per visible pair of those rows" % (len(rows), S, w.heads, dt),
+        "seconds": dt,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama7b_32k",
+                    help="llama7b_32k (default), packing_128k, video_text_256k, full_1m, tiny")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (HBM counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (asked for %d GPUs)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import long_context_blockwise_attn_amd as bw
+    from long_context_blockwise_attn_amd.inputs import WORKLOADS, make_qkv, packing
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = WORKLOADS[args.workload]
+    B, H, S, D = w.batch, w.heads, w.seqlen, w.head_dim
+    seg_np, pos_np, lengths = packing(w)
+    w.extra["lengths"] = lengths
+    q, k, v, do = make_qkv(w, device=dev, with_grad_out=True)
+    seg = None if seg_np is None else torch.from_numpy(seg_np).to(dev)
+    pos = torch.from_numpy(pos_np).to(dev)
+    do_bwd = w.backward
+
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    pf = bw.make_params(B, H, S, D, theta=w.theta, causal=w.causal, kv_chunk=w.kv_chunk)
+    ws_f = torch.empty(bw.workspace_bytes(pf, 0), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(bw.workspace_bytes(pf, 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        bw.attn_fwd(q, k, v, seg, pos, theta=w.theta, causal=w.causal, kv_chunk=w.kv_chunk, out=o, lse=lse,
+                    workspace=ws_f)
+        if do_bwd:
+            bw.attn_bwd(q, k, v, o, lse, do, seg, pos, theta=w.theta, causal=w.causal, kv_chunk=w.kv_chunk, dq=dq,
+                        dk=dk, dv=dv, workspace=ws_b)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # live per-kernel timing: HIP events recorded by the library around each
+    # launch, on the launch stream, over the timed region
+    lib = bw.load()
+    launches = {"rope": 4 if do_bwd else 2, "fwd": 1, "bwd_dq": 1 if do_bwd else 0, "bwd_dkdv": 1 if do_bwd else 0}
+    if w.theta <= 0:
+        launches["rope"] = 0
+    ev = {}
+    keep = []
+    for name, per in launches.items():
+        n = per * args.steps
+        if n == 0:
+            continue
+        st = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        sp = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in st + sp:
+            e.record()  # torch creates the underlying HIP event on first record
+        torch.cuda.synchronize()
+        arr_t = (ctypes.c_void_p * n)(*[e.cuda_event for e in st])
+        arr_p = (ctypes.c_void_p * n)(*[e.cuda_event for e in sp])
+        keep += [arr_t, arr_p]
+        rc = lib.attn_profile_events(KERNELS[name], arr_t, arr_p, n)
+        assert rc == 0
+        ev[name] = (st, sp)
+
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for _ in range(args.steps):
+        step()
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    kernel_ms = {}
+    for name, (st, sp) in ev.items():
+        cnt = lib.attn_profile_count(KERNELS[name])
+        times = [a.elapsed_time(b) for a, b in zip(st[:cnt], sp[:cnt])]
+        kernel_ms[name] = {"avg_ms": float(np.mean(times)), "launches_per_step": launches[name],
+                           "launches_timed": cnt}
+        lib.attn_profile_events(KERNELS[name], None, None, 0)
+
+    pairs = B * visible_pairs(lengths, w.causal)
+    fwd_flops = 4.0 * D * H * pairs
+    bwd_flops = 10.0 * D * H * pairs if do_bwd else 0.0
+    tflops = (fwd_flops + bwd_flops) / (ms_step * 1e-3) / 1e12
+
+    # dominant kernel and its roofline (MFMA bound): contractions it performs,
+    # 2*D FLOPs per visible pair each (fwd 2: QK^T, PV; dQ 3: QK^T, dP, dQ;
+    # dK/dV 4: QK^T, dP, dV, dK)
+    contractions = {"fwd": 2, "bwd_dq": 3, "bwd_dkdv": 4}
+    dom = max((n for n in contractions if n in kernel_ms),
+              key=lambda n: kernel_ms[n]["avg_ms"] * kernel_ms[n]["launches_per_step"])
+    dom_flops = contractions[dom] * 2.0 * D * H * pairs
+    dom_tflops = dom_flops / (kernel_ms[dom]["avg_ms"] * 1e-3) / 1e12
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": dom_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": dom_tflops / BF16_PEAK_TFLOPS, "traffic": None,
+                "flops_per_launch": dom_flops}
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        bcopy = torch.empty_like(a)
+        bcopy.copy_(a)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, q, k, v, do, seg_np, pos_np, args.cpu_seconds)
+
+    mask = "causal" + ("+segment" if seg_np is not None else "")
+    out = {
+        "metric": METRIC,
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "heads": H, "head_dim": D, "seq_len": S, "rope_theta": w.theta,
+                   "mask": mask, "kv_chunk": w.kv_chunk, "pass": "fwd+bwd" if do_bwd else "fwd",
+                   "visible_pairs": pairs, "parallelism": "single GPU"},
+        "pct_of_bf16_peak": 100.0 * tflops / BF16_PEAK_TFLOPS,
+        "fwd_tflops": fwd_flops / (kernel_ms["fwd"]["avg_ms"] * 1e-3) / 1e12,
+        "kernels_ms": {n: round(v["avg_ms"], 4) for n, v in kernel_ms.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

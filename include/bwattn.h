@@ -28,7 +28,8 @@
  *     stream).  The library never allocates, frees or synchronizes, and keeps
  *     no pointer after returning.  The caller owns every buffer, including the
  *     workspace sized by attn_workspace_bytes, and keeps them alive until the
- *     stream work has finished.  Entry points keep no state and are
+ *     stream work has finished.  Entry points keep no state (apart from the
+ *     thread-local measurement request of attn_profile_events) and are
  *     thread-safe.
  *   - Every argument is checked before any HIP call.  The return value is an
  *     attn_status; no exception crosses the ABI and the library never aborts.
@@ -116,6 +117,31 @@ int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, 
 int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v, const void* o,
              const float* lse, const void* d_o, const int32_t* segment_ids, const int32_t* positions,
              void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Measurement hook (for benchmarks and profilers; not needed to compute).    */
+/* ------------------------------------------------------------------------ */
+typedef enum {
+  ATTN_KERNEL_ROPE = 0,      /* RoPE pre-pass (also used by rope_apply)               */
+  ATTN_KERNEL_FWD = 1,       /* forward main kernel                                   */
+  ATTN_KERNEL_BWD_DQ = 2,    /* backward: dQ and Delta                                */
+  ATTN_KERNEL_BWD_DKDV = 3,  /* backward: dK and dV                                   */
+  ATTN_KERNEL_COUNT = 4
+} attn_kernel_id;
+
+/* Ask the library to bracket the next n launches of kernel `kernel` made by
+ * the calling thread with hipEventRecord(start[i], s) and
+ * hipEventRecord(stop[i], s), where s is the stream of the launch and i counts
+ * those launches from 0.  start and stop are arrays of n hipEvent_t created by
+ * the caller, which keeps them valid until the recorded work has finished.
+ * Launches after the n-th record nothing; n = 0 clears the request.  The
+ * request is thread-local and changes no result.  Returns ATTN_OK or
+ * ATTN_ERR_INVALID_ARG (kernel out of range, n < 0, null arrays with n > 0). */
+int attn_profile_events(int32_t kernel, void* const* start, void* const* stop, int32_t n);
+
+/* Number of launches of `kernel` bracketed so far under the current request
+ * of the calling thread (-1 if kernel is out of range). */
+int32_t attn_profile_count(int32_t kernel);
 
 #ifdef __cplusplus
 }

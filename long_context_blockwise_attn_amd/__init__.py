@@ -1,1 +1,188 @@
-"""Blockwise causal attention with RoPE and a packing mask for MI355X (gfx950)."""
+"""Blockwise exact causal attention with RoPE and a packing mask for MI355X.
+
+Thin ctypes binding over the C-ABI library ``libbwattn.so`` (include/bwattn.h):
+argument checks and marshalling only; every step of the computation runs in
+the library's HIP kernels.  PyTorch provides device memory and the stream.
+Importing this package does not load the library; the first call does, and
+fails loudly if the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["attn_fwd", "attn_bwd", "rope_apply", "workspace_bytes", "AttnError", "library_path", "Params"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libbwattn.so")
+_lib = None
+
+
+class AttnError(RuntimeError):
+    pass
+
+
+class Params(ctypes.Structure):
+    """attn_params of include/bwattn.h."""
+
+    _fields_ = [
+        ("struct_size", ctypes.c_int32),
+        ("batch", ctypes.c_int32),
+        ("heads", ctypes.c_int32),
+        ("seqlen", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+        ("causal", ctypes.c_int32),
+        ("rope_theta", ctypes.c_double),
+        ("kv_chunk", ctypes.c_int32),
+        ("deterministic", ctypes.c_int32),
+    ]
+
+
+def make_params(B, H, S, D, theta=0.0, causal=True, scale=0.0, kv_chunk=0, deterministic=False) -> Params:
+    return Params(ctypes.sizeof(Params), B, H, S, D, float(scale), int(bool(causal)), float(theta), int(kv_chunk),
+                  int(bool(deterministic)))
+
+
+def load():
+    """Load libbwattn.so (raises AttnError if it is missing)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise AttnError("HIP library %s is not built; run long_context_blockwise_attn_amd/build.py" % library_path)
+        lib = ctypes.CDLL(library_path)
+        P, V = ctypes.POINTER(Params), ctypes.c_void_p
+        lib.attn_status_string.restype = ctypes.c_char_p
+        lib.attn_status_string.argtypes = [ctypes.c_int]
+        lib.attn_last_error.restype = ctypes.c_char_p
+        lib.attn_last_error.argtypes = []
+        lib.attn_workspace_bytes.restype = ctypes.c_size_t
+        lib.attn_workspace_bytes.argtypes = [P, ctypes.c_int32]
+        lib.rope_apply.restype = ctypes.c_int
+        lib.rope_apply.argtypes = [P, V, V, V, ctypes.c_int32, V]
+        lib.attn_fwd.restype = ctypes.c_int
+        lib.attn_fwd.argtypes = [P, V, V, V, V, V, V, V, V, ctypes.c_size_t, V]
+        lib.attn_bwd.restype = ctypes.c_int
+        lib.attn_bwd.argtypes = [P, V, V, V, V, V, V, V, V, V, V, V, V, ctypes.c_size_t, V]
+        lib.attn_profile_events.restype = ctypes.c_int
+        lib.attn_profile_events.argtypes = [ctypes.c_int32, V, V, ctypes.c_int32]
+        lib.attn_profile_count.restype = ctypes.c_int32
+        lib.attn_profile_count.argtypes = [ctypes.c_int32]
+        _lib = lib
+    return _lib
+
+
+def _raise(rc):
+    if rc != 0:
+        lib = load()
+        raise AttnError("%s: %s" % (lib.attn_status_string(rc).decode(), lib.attn_last_error().decode()))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    import torch
+
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check_bhsd(name, t, shape=None):
+    import torch
+
+    if t.dtype != torch.bfloat16 or t.dim() != 4 or not t.is_contiguous() or not t.is_cuda:
+        raise AttnError("%s must be a contiguous bf16 CUDA tensor [B,H,S,D]" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise AttnError("%s has shape %r, expected %r" % (name, tuple(t.shape), tuple(shape)))
+
+
+def _check_bs(name, t, B, S):
+    import torch
+
+    if t is None:
+        return None
+    if t.dtype != torch.int32 or tuple(t.shape) != (B, S) or not t.is_contiguous() or not t.is_cuda:
+        raise AttnError("%s must be a contiguous int32 CUDA tensor [B,S]" % name)
+    return t
+
+
+def workspace_bytes(params: Params, which: int) -> int:
+    n = load().attn_workspace_bytes(ctypes.byref(params), which)
+    if n == 0:
+        _raise(1)
+    return int(n)
+
+
+def _workspace(params, which, workspace, device):
+    import torch
+
+    need = workspace_bytes(params, which)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def rope_apply(x, positions=None, theta=1e4, inverse=False, out=None):
+    """RoPE of x (bf16 [B,H,S,D]) at positions (int32 [B,S] or None)."""
+    import torch
+
+    _check_bhsd("x", x)
+    B, H, S, D = x.shape
+    _check_bs("positions", positions, B, S)
+    if out is None:
+        out = torch.empty_like(x)
+    _check_bhsd("out", out, x.shape)
+    p = make_params(B, H, S, D, theta=theta)
+    _raise(load().rope_apply(ctypes.byref(p), _ptr(x), _ptr(out), _ptr(positions), int(bool(inverse)), _stream()))
+    return out
+
+
+def attn_fwd(q, k, v, segment_ids=None, positions=None, theta=0.0, causal=True, scale=0.0, kv_chunk=0, out=None,
+             lse=None, workspace=None):
+    """Blockwise exact attention forward; returns (o bf16 [B,H,S,D], lse fp32 [B,H,S])."""
+    import torch
+
+    _check_bhsd("q", q)
+    B, H, S, D = q.shape
+    _check_bhsd("k", k, q.shape)
+    _check_bhsd("v", v, q.shape)
+    _check_bs("segment_ids", segment_ids, B, S)
+    _check_bs("positions", positions, B, S)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    _check_bhsd("out", out, q.shape)
+    p = make_params(B, H, S, D, theta=theta, causal=causal, scale=scale, kv_chunk=kv_chunk)
+    ws, nbytes = _workspace(p, 0, workspace, q.device)
+    _raise(load().attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(segment_ids), _ptr(positions), _ptr(out),
+                           _ptr(lse), _ptr(ws), nbytes, _stream()))
+    return out, lse
+
+
+def attn_bwd(q, k, v, o, lse, dout, segment_ids=None, positions=None, theta=0.0, causal=True, scale=0.0, kv_chunk=0,
+             dq=None, dk=None, dv=None, workspace=None):
+    """Backward of attn_fwd; returns (dq, dk, dv) bf16 [B,H,S,D] with respect to
+    the un-rotated q and k and to v."""
+    import torch
+
+    _check_bhsd("q", q)
+    B, H, S, D = q.shape
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _check_bhsd(name, t, q.shape)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, S) or not lse.is_contiguous():
+        raise AttnError("lse must be a contiguous fp32 tensor [B,H,S]")
+    _check_bs("segment_ids", segment_ids, B, S)
+    _check_bs("positions", positions, B, S)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_bhsd(name, t, q.shape)
+    p = make_params(B, H, S, D, theta=theta, causal=causal, scale=scale, kv_chunk=kv_chunk)
+    ws, nbytes = _workspace(p, 1, workspace, q.device)
+    _raise(load().attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                           _ptr(segment_ids), _ptr(positions), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), nbytes,
+                           _stream()))
+    return dq, dk, dv

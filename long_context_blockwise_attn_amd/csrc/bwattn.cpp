@@ -1,0 +1,392 @@
+// C-ABI entry points: argument checks (before any HIP call), workspace plan,
+// and the launch sequence of each operation.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "bwattn.h"
+#include "kernels.hpp"
+
+using namespace bwattn;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+// Measurement hook state (thread-local): events to record around launches.
+struct ProfileSlot {
+  void* const* start = nullptr;
+  void* const* stop = nullptr;
+  int32_t n = 0, used = 0;
+};
+thread_local ProfileSlot g_prof[ATTN_KERNEL_COUNT];
+
+// Launch wrapper: records the requested events around one kernel launch.
+template <typename F>
+hipError_t timed_launch(int kernel, hipStream_t st, F&& launch) {
+  ProfileSlot& ps = g_prof[kernel];
+  bool rec = ps.used < ps.n;
+  if (rec) {
+    hipError_t e = hipEventRecord((hipEvent_t)ps.start[ps.used], st);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = launch();
+  if (e != hipSuccess) return e;
+  if (rec) {
+    e = hipEventRecord((hipEvent_t)ps.stop[ps.used], st);
+    if (e != hipSuccess) return e;
+    ++ps.used;
+  }
+  return hipSuccess;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+constexpr int64_t kMaxSeq = int64_t(1) << 24;  // per-head offsets stay below 2^32 bytes
+
+int check_params(const attn_params* p) {
+  if (p == nullptr) return fail(ATTN_ERR_INVALID_ARG, "params is NULL");
+  if (p->struct_size != (int32_t)sizeof(attn_params))
+    return fail(ATTN_ERR_INVALID_ARG, "struct_size %d != sizeof(attn_params) %d", p->struct_size,
+                (int)sizeof(attn_params));
+  if (p->batch < 1 || p->heads < 1 || p->seqlen < 1 || p->head_dim < 1)
+    return fail(ATTN_ERR_INVALID_ARG, "batch, heads, seqlen and head_dim must be >= 1 (got %d, %d, %d, %d)",
+                p->batch, p->heads, p->seqlen, p->head_dim);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(ATTN_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", p->head_dim);
+  if ((int64_t)p->seqlen > kMaxSeq) return fail(ATTN_ERR_INVALID_ARG, "seqlen %d above %lld", p->seqlen, (long long)kMaxSeq);
+  int64_t bh = (int64_t)p->batch * p->heads;
+  if (bh > (int64_t)1 << 20) return fail(ATTN_ERR_INVALID_ARG, "batch*heads %lld too large", (long long)bh);
+  int64_t elems = bh * p->seqlen * p->head_dim;
+  if (elems > ((int64_t)1 << 40)) return fail(ATTN_ERR_INVALID_ARG, "tensor of %lld elements too large", (long long)elems);
+  int64_t tiles = bh * ((p->seqlen + kFwdBlockQ - 1) / kFwdBlockQ);
+  if (tiles > ((int64_t)1 << 31) - 1) return fail(ATTN_ERR_INVALID_ARG, "too many tiles");
+  if (p->causal != 0 && p->causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (p->deterministic != 0 && p->deterministic != 1) return fail(ATTN_ERR_INVALID_ARG, "deterministic must be 0 or 1");
+  if (!(std::isfinite(p->softmax_scale))) return fail(ATTN_ERR_INVALID_ARG, "softmax_scale is not finite");
+  if (std::isnan(p->rope_theta) || std::isinf(p->rope_theta))
+    return fail(ATTN_ERR_INVALID_ARG, "rope_theta is not finite");
+  if (p->kv_chunk < 0 || p->kv_chunk % kFwdBlockK != 0)
+    return fail(ATTN_ERR_INVALID_ARG, "kv_chunk %d must be 0 or a positive multiple of %d", p->kv_chunk, kFwdBlockK);
+  return ATTN_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Plan {
+  int B, H, S, D;
+  bool rope, seg;
+  int nblk, n_qtiles, n_ktiles, n_bkv, n_bq;
+  size_t off_qr, off_kr, off_delta, off_blk, off_qrange, off_krange, total;
+};
+
+// Workspace layout.  The segment-dependent parts are always reserved so that
+// the size depends only on the parameters.
+Plan make_plan(const attn_params* p, int which) {
+  Plan pl{};
+  pl.B = p->batch;
+  pl.H = p->heads;
+  pl.S = p->seqlen;
+  pl.D = p->head_dim;
+  pl.rope = p->rope_theta > 0.0;
+  pl.nblk = (pl.S + kSegBlock - 1) / kSegBlock;
+  pl.n_qtiles = (pl.S + kFwdBlockQ - 1) / kFwdBlockQ;
+  pl.n_ktiles = (pl.S + kFwdBlockK - 1) / kFwdBlockK;
+  pl.n_bkv = (pl.S + kBwdBlockK - 1) / kBwdBlockK;
+  pl.n_bq = (pl.S + kBwdBlockQ - 1) / kBwdBlockQ;
+  size_t n = (size_t)pl.B * pl.H * pl.S * pl.D;
+  size_t off = 0;
+  if (pl.rope) {
+    pl.off_qr = off;
+    off += align256(n * 2);
+    pl.off_kr = off;
+    off += align256(n * 2);
+  }
+  if (which == 1) {
+    pl.off_delta = off;
+    off += align256((size_t)pl.B * pl.H * pl.S * 4);
+  }
+  pl.off_blk = off;
+  off += align256((size_t)pl.B * pl.nblk * sizeof(int2));
+  pl.off_qrange = off;
+  off += align256((size_t)pl.B * pl.n_qtiles * sizeof(int2));
+  if (which == 1) {
+    pl.off_krange = off;
+    off += align256((size_t)pl.B * pl.n_bkv * sizeof(int2));
+  }
+  pl.total = off;
+  return pl;
+}
+
+// Device check, cached per device: the kernels are built for gfx950 only.
+int check_device() {
+  static std::mutex mu;
+  static int state[64];  // 0 unknown, 1 ok, 2 unsupported
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(ATTN_ERR_HIP, "hipGetDevice failed");
+  if (dev < 0 || dev >= 64) return fail(ATTN_ERR_HIP, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (state[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return fail(ATTN_ERR_HIP, "hipGetDeviceProperties failed");
+    state[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+  }
+  if (state[dev] != 1) return fail(ATTN_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+  return ATTN_OK;
+}
+
+void fill_turns(double* turns, int D, double theta) {
+  for (int i = 0; i < D / 2; ++i) turns[i] = std::pow(theta, -2.0 * i / D) / (2.0 * M_PI);
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ATTN_OK;
+}
+
+float scale_of(const attn_params* p) {
+  return p->softmax_scale > 0.f ? p->softmax_scale : (float)(1.0 / std::sqrt((double)p->head_dim));
+}
+
+// RoPE of q and k into the workspace, and the segment schedule.
+int prepare(const attn_params* p, const Plan& pl, const void* q, const void* k, const int32_t* seg,
+            const int32_t* pos, char* ws, bool bwd, hipStream_t st) {
+  if (pl.rope) {
+    RopeArgs r{};
+    r.pos = pos;
+    r.B = pl.B;
+    r.H = pl.H;
+    r.S = pl.S;
+    r.D = pl.D;
+    r.inverse = 0;
+    fill_turns(r.turns, pl.D, p->rope_theta);
+    r.x = (const uint16_t*)q;
+    r.y = (uint16_t*)(ws + pl.off_qr);
+    int rc = hip_status(timed_launch(ATTN_KERNEL_ROPE, st, [&] { return launch_rope(r, st); }), "rope(q) launch");
+    if (rc) return rc;
+    r.x = (const uint16_t*)k;
+    r.y = (uint16_t*)(ws + pl.off_kr);
+    rc = hip_status(timed_launch(ATTN_KERNEL_ROPE, st, [&] { return launch_rope(r, st); }), "rope(k) launch");
+    if (rc) return rc;
+  }
+  if (seg) {
+    int2* blk = (int2*)(ws + pl.off_blk);
+    int rc = hip_status(launch_block_ranges(seg, pl.B, pl.S, pl.nblk, blk, st), "segment ranges launch");
+    if (rc) return rc;
+    TileRangeArgs t{};
+    t.blk = blk;
+    t.B = pl.B;
+    t.S = pl.S;
+    t.nblk = pl.nblk;
+    t.causal = p->causal;
+    // query tiles -> K/V tile ranges (forward and dQ)
+    t.out = (int2*)(ws + pl.off_qrange);
+    t.own_rows = kFwdBlockQ;
+    t.other_rows = kFwdBlockK;
+    t.n_own = pl.n_qtiles;
+    t.n_other = pl.n_ktiles;
+    t.own_is_query = 1;
+    rc = hip_status(launch_tile_ranges(t, st), "tile ranges launch");
+    if (rc) return rc;
+    if (bwd) {
+      // key tiles -> query tile ranges (dK/dV)
+      t.out = (int2*)(ws + pl.off_krange);
+      t.own_rows = kBwdBlockK;
+      t.other_rows = kBwdBlockQ;
+      t.n_own = pl.n_bkv;
+      t.n_other = pl.n_bq;
+      t.own_is_query = 0;
+      rc = hip_status(launch_tile_ranges(t, st), "key tile ranges launch");
+      if (rc) return rc;
+    }
+  }
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_ERR_INVALID_ARG: return "ATTN_ERR_INVALID_ARG";
+    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED";
+    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE";
+    case ATTN_ERR_HIP: return "ATTN_ERR_HIP";
+    default: return "ATTN_ERR_UNKNOWN";
+  }
+}
+
+const char* attn_last_error(void) { return g_err; }
+
+size_t attn_workspace_bytes(const attn_params* p, int32_t which) {
+  if (check_params(p) != ATTN_OK) return 0;
+  if (which != 0 && which != 1) {
+    fail(ATTN_ERR_INVALID_ARG, "which must be 0 (forward) or 1 (backward)");
+    return 0;
+  }
+  g_err[0] = 0;
+  return make_plan(p, which).total;
+}
+
+int rope_apply(const attn_params* p, const void* x, void* y, const int32_t* positions, int32_t inverse,
+               void* stream) {
+  int rc = check_params(p);
+  if (rc) return rc;
+  if (!(p->rope_theta > 0.0)) return fail(ATTN_ERR_INVALID_ARG, "rope_apply needs rope_theta > 0");
+  if (x == nullptr || y == nullptr) return fail(ATTN_ERR_INVALID_ARG, "x and y must not be NULL");
+  if (!aligned16(x) || !aligned16(y) || !aligned16(positions))
+    return fail(ATTN_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  if (inverse != 0 && inverse != 1) return fail(ATTN_ERR_INVALID_ARG, "inverse must be 0 or 1");
+  rc = check_device();
+  if (rc) return rc;
+  RopeArgs r{};
+  r.x = (const uint16_t*)x;
+  r.y = (uint16_t*)y;
+  r.pos = positions;
+  r.B = p->batch;
+  r.H = p->heads;
+  r.S = p->seqlen;
+  r.D = p->head_dim;
+  r.inverse = inverse;
+  fill_turns(r.turns, p->head_dim, p->rope_theta);
+  hipStream_t st = (hipStream_t)stream;
+  rc = hip_status(timed_launch(ATTN_KERNEL_ROPE, st, [&] { return launch_rope(r, st); }), "rope launch");
+  if (rc) return rc;
+  g_err[0] = 0;
+  return ATTN_OK;
+}
+
+int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, const int32_t* segment_ids,
+             const int32_t* positions, void* o, float* lse, void* workspace, size_t workspace_bytes,
+             void* stream) {
+  int rc = check_params(p);
+  if (rc) return rc;
+  if (!q || !k || !v || !o || !lse) return fail(ATTN_ERR_INVALID_ARG, "q, k, v, o and lse must not be NULL");
+  const void* ptrs[] = {q, k, v, o, lse, segment_ids, positions, workspace};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return fail(ATTN_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  Plan pl = make_plan(p, 0);
+  if (workspace == nullptr || workspace_bytes < pl.total)
+    return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", pl.total, workspace_bytes,
+                workspace ? "" : " (NULL)");
+  rc = check_device();
+  if (rc) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  rc = prepare(p, pl, q, k, segment_ids, positions, ws, false, st);
+  if (rc) return rc;
+  FwdArgs a{};
+  a.q = pl.rope ? (const uint16_t*)(ws + pl.off_qr) : (const uint16_t*)q;
+  a.k = pl.rope ? (const uint16_t*)(ws + pl.off_kr) : (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.o = (uint16_t*)o;
+  a.lse = lse;
+  a.seg = segment_ids;
+  a.blk = segment_ids ? (const int2*)(ws + pl.off_blk) : nullptr;
+  a.qrange = segment_ids ? (const int2*)(ws + pl.off_qrange) : nullptr;
+  a.B = pl.B;
+  a.H = pl.H;
+  a.S = pl.S;
+  a.n_qtiles = pl.n_qtiles;
+  a.n_ktiles = pl.n_ktiles;
+  a.nblk = pl.nblk;
+  a.scale_log2 = scale_of(p) * 1.4426950408889634f;
+  a.causal = p->causal;
+  a.chunk_tiles = p->kv_chunk / kFwdBlockK;
+  rc = hip_status(timed_launch(ATTN_KERNEL_FWD, st, [&] { return launch_attn_fwd(a, pl.D, st); }), "attn_fwd launch");
+  if (rc) return rc;
+  g_err[0] = 0;
+  return ATTN_OK;
+}
+
+int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* d_o, const int32_t* segment_ids, const int32_t* positions, void* dq, void* dk, void* dv,
+             void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_params(p);
+  if (rc) return rc;
+  if (!q || !k || !v || !o || !lse || !d_o || !dq || !dk || !dv)
+    return fail(ATTN_ERR_INVALID_ARG, "q, k, v, o, lse, d_o, dq, dk and dv must not be NULL");
+  const void* ptrs[] = {q, k, v, o, lse, d_o, segment_ids, positions, dq, dk, dv, workspace};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return fail(ATTN_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  Plan pl = make_plan(p, 1);
+  if (workspace == nullptr || workspace_bytes < pl.total)
+    return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", pl.total, workspace_bytes,
+                workspace ? "" : " (NULL)");
+  rc = check_device();
+  if (rc) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  rc = prepare(p, pl, q, k, segment_ids, positions, ws, true, st);
+  if (rc) return rc;
+  BwdArgs a{};
+  a.q = pl.rope ? (const uint16_t*)(ws + pl.off_qr) : (const uint16_t*)q;
+  a.k = pl.rope ? (const uint16_t*)(ws + pl.off_kr) : (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.o = (const uint16_t*)o;
+  a.dout = (const uint16_t*)d_o;
+  a.lse = lse;
+  a.delta = (float*)(ws + pl.off_delta);
+  a.dq = (uint16_t*)dq;
+  a.dk = (uint16_t*)dk;
+  a.dv = (uint16_t*)dv;
+  a.seg = segment_ids;
+  a.pos = positions;
+  a.blk = segment_ids ? (const int2*)(ws + pl.off_blk) : nullptr;
+  a.qrange = segment_ids ? (const int2*)(ws + pl.off_qrange) : nullptr;
+  a.krange = segment_ids ? (const int2*)(ws + pl.off_krange) : nullptr;
+  a.B = pl.B;
+  a.H = pl.H;
+  a.S = pl.S;
+  a.n_qtiles = pl.n_qtiles;
+  a.n_ktiles = pl.n_ktiles;
+  a.nblk = pl.nblk;
+  a.n_bkv = pl.n_bkv;
+  a.n_bq = pl.n_bq;
+  a.scale = scale_of(p);
+  a.scale_log2 = a.scale * 1.4426950408889634f;
+  a.causal = p->causal;
+  a.chunk_tiles = p->kv_chunk / kFwdBlockK;
+  a.rope = pl.rope ? 1 : 0;
+  if (pl.rope) fill_turns(a.turns, pl.D, p->rope_theta);
+  // dQ first: it also forms Delta = <dO, O> per row, which dK/dV reads
+  rc = hip_status(timed_launch(ATTN_KERNEL_BWD_DQ, st, [&] { return launch_attn_bwd_dq(a, pl.D, st); }), "attn_bwd dq launch");
+  if (rc) return rc;
+  rc = hip_status(timed_launch(ATTN_KERNEL_BWD_DKDV, st, [&] { return launch_attn_bwd_dkdv(a, pl.D, st); }), "attn_bwd dkdv launch");
+  if (rc) return rc;
+  g_err[0] = 0;
+  return ATTN_OK;
+}
+
+int attn_profile_events(int32_t kernel, void* const* start, void* const* stop, int32_t n) {
+  if (kernel < 0 || kernel >= ATTN_KERNEL_COUNT) return fail(ATTN_ERR_INVALID_ARG, "kernel id %d out of range", kernel);
+  if (n < 0) return fail(ATTN_ERR_INVALID_ARG, "n must be >= 0");
+  if (n > 0 && (start == nullptr || stop == nullptr)) return fail(ATTN_ERR_INVALID_ARG, "event arrays must not be NULL");
+  g_prof[kernel].start = n > 0 ? start : nullptr;
+  g_prof[kernel].stop = n > 0 ? stop : nullptr;
+  g_prof[kernel].n = n;
+  g_prof[kernel].used = 0;
+  g_err[0] = 0;
+  return ATTN_OK;
+}
+
+int32_t attn_profile_count(int32_t kernel) {
+  if (kernel < 0 || kernel >= ATTN_KERNEL_COUNT) return -1;
+  return g_prof[kernel].used;
+}
+
+}  // extern "C"

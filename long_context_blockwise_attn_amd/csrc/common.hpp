@@ -1,0 +1,59 @@
+// Device-side helpers shared by the HIP kernels of the library (gfx950 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bwattn {
+
+typedef uint16_t bf16_t;  // raw bf16 bits in memory
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  f32x2 f = {a, b};
+  bf16x2 h = __builtin_convertvector(f, bf16x2);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Value held by the lane 32 positions away (lanes l and l^32 swap).
+__device__ __forceinline__ float swap_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Workgroup order for long-to-short scheduling with heads grouped per XCD.
+// Workgroups are handed to the 8 XCDs round robin; when the number of (b,h)
+// slices is a multiple of 8, all tiles of one slice go to one XCD so that its
+// concurrent workgroups share K/V in that XCD's L2.  Tiles are issued in the
+// order given by `rank` (0 = first).  The map is a bijection in every case.
+__device__ __forceinline__ void xcd_tile_order(int bid, int n_bh, int n_tiles, int& bh, int& rank) {
+  if ((n_bh & 7) == 0) {
+    int xcd = bid & 7, j = bid >> 3;
+    int per = n_bh >> 3;
+    rank = j / per;
+    bh = xcd + 8 * (j - rank * per);
+  } else {
+    rank = bid / n_bh;
+    bh = bid - rank * n_bh;
+  }
+}
+
+}  // namespace bwattn

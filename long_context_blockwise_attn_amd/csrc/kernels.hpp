@@ -1,0 +1,84 @@
+// Kernel argument blocks and launchers of the library (host and device).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bwattn {
+
+// Tile sizes shared by the host schedule and the kernels.
+constexpr int kFwdBlockQ = 256;   // query rows per forward / dQ workgroup (4 waves x 64 rows)
+constexpr int kFwdBlockK = 64;    // keys per K/V tile streamed by the forward / dQ kernels
+constexpr int kBwdBlockK = 128;   // keys per dK/dV workgroup (4 waves x 32 keys)
+constexpr int kBwdBlockQ = 64;    // query rows per Q/dO tile streamed by the dK/dV kernel
+constexpr int kSegBlock = 32;     // rows per segment-range block
+
+struct RopeArgs {
+  const uint16_t* x;
+  uint16_t* y;
+  const int32_t* pos;  // [B,S] or null (pos = s)
+  int B, H, S, D;
+  int inverse;
+  double turns[64];  // theta^(-2i/D) / (2 pi), i < D/2
+};
+
+struct TileRangeArgs {
+  const int2* blk;  // [B, nblk] segment ranges or null (no packing mask)
+  int2* out;        // [B, n_own] -> [lo, hi) over the other side's tiles
+  int B, S, nblk;
+  int own_rows, other_rows, n_own, n_other;
+  int causal, own_is_query;
+};
+
+// Forward and dQ kernels: a workgroup owns kFwdBlockQ query rows of one (b,h)
+// and streams K/V tiles of kFwdBlockK keys.
+struct FwdArgs {
+  const uint16_t* q;  // rotated queries [B,H,S,D]
+  const uint16_t* k;  // rotated keys
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;          // natural log, [B,H,S]
+  const int32_t* seg;  // [B,S] or null
+  const int2* blk;     // segment ranges per 32 rows, or null
+  const int2* qrange;  // [B, n_qtiles] K/V tile range, or null
+  int B, H, S;
+  int n_qtiles, n_ktiles, nblk;
+  float scale_log2;    // softmax scale * log2(e)
+  int causal;
+  int chunk_tiles;     // ring chunk in K/V tiles; 0 = natural order
+};
+
+struct BwdArgs {
+  const uint16_t* q;   // rotated queries
+  const uint16_t* k;   // rotated keys
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;    // natural log
+  float* delta;        // [B,H,S] workspace: <dO_i, O_i>
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  const int32_t* seg;
+  const int32_t* pos;  // [B,S] or null, for the RoPE backward
+  const int2* blk;
+  const int2* qrange;   // per query tile (dQ kernel): K/V tile range
+  const int2* krange;   // per key tile (dK/dV kernel): query tile range
+  int B, H, S;
+  int n_qtiles, n_ktiles, nblk;
+  int n_bkv, n_bq;     // dK/dV kernel: key tiles of kBwdBlockK and query tiles of kBwdBlockQ
+  float scale;         // softmax scale
+  float scale_log2;
+  int causal;
+  int chunk_tiles;
+  int rope;            // apply the RoPE backward
+  double turns[64];
+};
+
+hipError_t launch_rope(const RopeArgs& a, hipStream_t st);
+hipError_t launch_block_ranges(const int32_t* seg, int B, int S, int nblk, int2* out, hipStream_t st);
+hipError_t launch_tile_ranges(const TileRangeArgs& a, hipStream_t st);
+hipError_t launch_attn_fwd(const FwdArgs& a, int D, hipStream_t st);
+hipError_t launch_attn_bwd_dq(const BwdArgs& a, int D, hipStream_t st);
+hipError_t launch_attn_bwd_dkdv(const BwdArgs& a, int D, hipStream_t st);
+
+}  // namespace bwattn

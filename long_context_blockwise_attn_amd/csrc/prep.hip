@@ -1,0 +1,166 @@
+// RoPE and tile-schedule kernels.
+//
+// RoPE ("standard RoPE" with a context-scaled base theta: zhao9797 page
+// "LWM (Large World Model)", 模型架构 and the Stage I table of 训练方法; read as
+// RoFormer's rotation of adjacent pairs): pair i of a row at position pos turns
+// by pos * theta^(-2i/D).  Positions reach 2^20 and theta 5e7, so the angle is
+// formed and reduced to one turn in fp64 before the fp32 sine and cosine.
+//
+// Tile schedule (masked sequence packing: each packed example attends only to
+// itself, 训练方法): per 32-row block the min and max segment id, and per tile
+// the range of tiles on the other side that can hold a visible pair.  A pair
+// of tiles whose segment-id ranges do not intersect has no visible pair, which
+// holds for any int32 ids; the range is tight when documents are contiguous.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace bwattn {
+
+// One thread per (b, s, group of 4 pairs); it forms the 4 angles once and
+// rotates that group in every head, so the fp64 work is shared by H rows.
+__global__ void rope_kernel(RopeArgs a) {
+  const int groups = a.D / 8;
+  int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int64_t total = (int64_t)a.B * a.S * groups;
+  if (tid >= total) return;
+  int g = (int)(tid % groups);
+  int64_t bs = tid / groups;
+  int s = (int)(bs % a.S);
+  int b = (int)(bs / a.S);
+  double pos = a.pos ? (double)a.pos[bs] : (double)s;
+  float c[4], sn[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    double rev = pos * a.turns[4 * g + i];  // angle in turns
+    rev -= rint(rev);                       // reduce to [-1/2, 1/2] in fp64
+    float f = (float)rev;
+    c[i] = __builtin_amdgcn_cosf(f);       // cos(2*pi*f)
+    sn[i] = __builtin_amdgcn_sinf(f);
+    if (a.inverse) sn[i] = -sn[i];
+  }
+  const int64_t head_stride = (int64_t)a.S * a.D;
+  int64_t off = ((int64_t)b * a.H * a.S + s) * a.D + 8 * g;
+  for (int h = 0; h < a.H; ++h, off += head_stride) {
+    u32x4 x = *(const u32x4*)(a.x + off);
+    u32x4 y;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float x0 = bf16_lo(x[i]), x1 = bf16_hi(x[i]);
+      float y0 = x0 * c[i] - x1 * sn[i];
+      float y1 = x0 * sn[i] + x1 * c[i];
+      y[i] = pack_bf16x2(y0, y1);
+    }
+    *(u32x4*)(a.y + off) = y;
+  }
+}
+
+// Min and max segment id of every 32-row block of every batch row.
+__global__ void block_range_kernel(const int32_t* seg, int B, int S, int nblk, int2* out) {
+  int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (tid >= (int64_t)B * nblk) return;
+  int blk = (int)(tid % nblk);
+  int b = (int)(tid / nblk);
+  int r0 = blk * 32, r1 = min(S, r0 + 32);
+  const int32_t* sb = seg + (int64_t)b * S;
+  int mn = sb[r0], mx = sb[r0];
+  for (int r = r0 + 1; r < r1; ++r) {
+    mn = min(mn, sb[r]);
+    mx = max(mx, sb[r]);
+  }
+  out[tid] = make_int2(mn, mx);
+}
+
+__device__ __forceinline__ int2 rows_range(const int2* br, int nblk, int r0, int rows) {
+  int b0 = r0 >> 5, b1 = min(nblk, (r0 + rows + 31) >> 5);
+  int2 acc = br[b0];
+  for (int k = b0 + 1; k < b1; ++k) {
+    int2 v = br[k];
+    acc.x = min(acc.x, v.x);
+    acc.y = max(acc.y, v.y);
+  }
+  return acc;
+}
+
+// One wave per (b, own tile).  Writes [lo, hi) over the other side's tiles:
+// the first and one past the last tile whose segment range meets the own
+// tile's, within the causal candidates.  own_is_query selects which side of
+// the causal condition the own tile is on.
+__global__ void tile_range_kernel(TileRangeArgs a) {
+  int wid = (int)((blockIdx.x * (int64_t)blockDim.x + threadIdx.x) >> 6);
+  int lane = threadIdx.x & 63;
+  if (wid >= a.B * a.n_own) return;
+  int t = wid % a.n_own;
+  int b = wid / a.n_own;
+  int own0 = t * a.own_rows;
+  int own1 = min(a.S, own0 + a.own_rows);  // exclusive
+  int c_lo = 0, c_hi = a.n_other;
+  if (a.causal) {
+    if (a.own_is_query)
+      c_hi = min(a.n_other, (own1 - 1) / a.other_rows + 1);
+    else
+      c_lo = own0 / a.other_rows;
+  }
+  int lo = c_lo, hi = c_hi;
+  if (a.blk != nullptr && c_lo < c_hi) {
+    const int2* br = a.blk + (int64_t)b * a.nblk;
+    int2 own = rows_range(br, a.nblk, own0, own1 - own0);
+    lo = c_hi;
+    for (int base = c_lo; base < c_hi; base += 64) {
+      int c = base + lane;
+      bool hit = false;
+      if (c < c_hi) {
+        int2 o = rows_range(br, a.nblk, c * a.other_rows, a.other_rows);
+        hit = !(o.y < own.x || o.x > own.y);
+      }
+      unsigned long long m = __ballot(hit);
+      if (m) {
+        lo = base + __ffsll((long long)m) - 1;
+        break;
+      }
+    }
+    hi = lo;
+    for (int top = c_hi; top > lo; top -= 64) {
+      int c = top - 1 - lane;
+      bool hit = false;
+      if (c >= lo) {
+        int2 o = rows_range(br, a.nblk, c * a.other_rows, a.other_rows);
+        hit = !(o.y < own.x || o.x > own.y);
+      }
+      unsigned long long m = __ballot(hit);
+      if (m) {
+        hi = top - (__ffsll((long long)m) - 1);
+        break;
+      }
+    }
+  }
+  if (lane == 0) a.out[wid] = make_int2(lo, hi);
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_rope(const RopeArgs& a, hipStream_t st) {
+  int64_t total = (int64_t)a.B * a.S * (a.D / 8);
+  int threads = 256;
+  int64_t blocks = (total + threads - 1) / threads;
+  hipLaunchKernelGGL(rope_kernel, dim3((unsigned)blocks), dim3(threads), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_ranges(const int32_t* seg, int B, int S, int nblk, int2* out, hipStream_t st) {
+  int64_t total = (int64_t)B * nblk;
+  int threads = 256;
+  hipLaunchKernelGGL(block_range_kernel, dim3((unsigned)((total + threads - 1) / threads)), dim3(threads), 0, st,
+                     seg, B, S, nblk, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_ranges(const TileRangeArgs& a, hipStream_t st) {
+  int64_t waves = (int64_t)a.B * a.n_own;
+  int threads = 256;
+  int64_t blocks = (waves * 64 + threads - 1) / threads;
+  hipLaunchKernelGGL(tile_range_kernel, dim3((unsigned)blocks), dim3(threads), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace bwattn

@@ -1,0 +1,104 @@
+"""The C-ABI library loads, exports every entry point of include/bwattn.h, and
+rejects bad arguments before touching the GPU (no compute call here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import long_context_blockwise_attn_amd as bw
+
+    if not os.path.exists(bw.library_path):
+        from long_context_blockwise_attn_amd import build
+
+        build.build()
+    return bw.load()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "bwattn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_]+)\s*\([^;{]*\)\s*;", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"attn_fwd", "attn_bwd", "rope_apply", "attn_workspace_bytes", "attn_status_string",
+            "attn_last_error", "attn_profile_events", "attn_profile_count"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_params_layout_matches_header():
+    import long_context_blockwise_attn_amd as bw
+
+    # int32 x5, float, int32, (pad), double, int32 x2 -> 48 bytes with 8-byte alignment
+    assert ctypes.sizeof(bw.Params) == 48
+    assert bw.Params.rope_theta.offset == 32
+
+
+def call_fwd(lib, p, q=16, k=32, v=48, seg=None, pos=None, o=64, lse=80, ws=None, nbytes=0):
+    V = ctypes.c_void_p
+    return lib.attn_fwd(ctypes.byref(p) if p is not None else None, V(q) if q else None, V(k) if k else None,
+                        V(v) if v else None, V(seg) if seg else None, V(pos) if pos else None, V(o) if o else None,
+                        V(lse) if lse else None, V(ws) if ws else None, nbytes, None)
+
+
+def test_argument_errors_before_any_hip_call(lib):
+    import long_context_blockwise_attn_amd as bw
+
+    ok = bw.make_params(1, 2, 1024, 128, theta=1e6)
+    assert call_fwd(lib, None) == 1
+    bad = bw.make_params(1, 2, 1024, 128)
+    bad.struct_size = 40
+    assert call_fwd(lib, bad) == 1 and b"struct_size" in lib.attn_last_error()
+    assert call_fwd(lib, bw.make_params(0, 2, 1024, 128)) == 1
+    assert call_fwd(lib, bw.make_params(1, 2, 0, 128)) == 1
+    assert call_fwd(lib, bw.make_params(1, 2, 1024, 96)) == 2
+    assert call_fwd(lib, bw.make_params(1, 2, 1024, 128, kv_chunk=100)) == 1
+    assert call_fwd(lib, bw.make_params(1, 2, 1024, 128, theta=float("nan"))) == 1
+    p = bw.make_params(1, 2, 1024, 128)
+    p.causal = 2
+    assert call_fwd(lib, p) == 1
+    assert call_fwd(lib, ok, q=0) == 1
+    assert call_fwd(lib, ok, q=18) == 1 and b"aligned" in lib.attn_last_error()
+    assert call_fwd(lib, ok, ws=None) == 3
+    assert call_fwd(lib, ok, ws=4096, nbytes=16) == 3
+    assert lib.attn_status_string(3) == b"ATTN_ERR_WORKSPACE"
+    V = ctypes.c_void_p
+    assert lib.rope_apply(ctypes.byref(bw.make_params(1, 1, 8, 64, theta=0.0)), V(16), V(16), None, 0, None) == 1
+    assert lib.rope_apply(ctypes.byref(ok), V(16), V(16), None, 2, None) == 1
+    # attn_bwd(p, q, k, v, o, lse, d_o, seg, pos, dq, dk, dv, ws, ws_bytes, stream)
+    args = [ctypes.byref(ok)] + [V(16 * (i + 1)) for i in range(12)] + [0, None]
+    args[7] = None  # segment_ids may be NULL
+    args[8] = None  # positions may be NULL
+    args[12] = None
+    assert lib.attn_bwd(*args) == 3  # no workspace
+    args[5] = None  # lse is required
+    assert lib.attn_bwd(*args) == 1
+
+
+def test_workspace_size_depends_only_on_params(lib):
+    import long_context_blockwise_attn_amd as bw
+
+    p = bw.make_params(1, 32, 32768, 128, theta=1e6)
+    f, b = bw.workspace_bytes(p, 0), bw.workspace_bytes(p, 1)
+    n = 32 * 32768 * 128
+    assert f >= 2 * n * 2 and b >= 2 * n * 2 + 32 * 32768 * 4
+    p0 = bw.make_params(1, 32, 32768, 128, theta=0.0)
+    assert bw.workspace_bytes(p0, 0) < f
+    assert lib.attn_workspace_bytes(ctypes.byref(p), 7) == 0
+
+
+def test_profile_hook_arguments(lib):
+    assert lib.attn_profile_events(9, None, None, 0) == 1
+    assert lib.attn_profile_events(1, None, None, -1) == 1
+    assert lib.attn_profile_events(1, None, None, 3) == 1
+    assert lib.attn_profile_events(1, None, None, 0) == 0
+    assert lib.attn_profile_count(1) == 0
+    assert lib.attn_profile_count(17) == -1
