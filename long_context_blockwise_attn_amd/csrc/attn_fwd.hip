@@ -7,30 +7,33 @@
 // summary page: no approximation).  Masks: causal (decoder-only model) and
 // the packing mask (each packed example attends only to itself, 训练方法).
 //
-// Work decomposition: a workgroup of 4 waves owns 256 query rows of one
-// (batch, head); each wave owns 64 rows (two groups of 32).  K/V tiles of 64
-// keys are double-buffered in LDS.  Scores are computed transposed,
-// S^T = K Q^T, so each lane holds one query row: the row max needs one
-// exchange between lanes l and l^32, and the running rescale of O is a
-// per-lane scalar.  O^T = V^T P^T takes P^T straight from the score registers
-// (the key order inside each 16-key slab is permuted consistently on both
-// operands) and V^T through the LDS transposing read.
+// Work decomposition: a workgroup of NW waves owns 256 query rows of one
+// (batch, head); each wave owns 32 * QG rows.  Tiles of 64 keys of K and of
+// the transposed V are double-buffered in LDS and filled by direct
+// global-to-LDS loads.  Scores are computed transposed, S^T = K Q^T, so each
+// lane holds one query row: the row max needs one exchange between lanes l
+// and l^32, and the running rescale of O is a per-lane scalar.
+// O^T = V^T P^T takes P^T straight from the score registers; the transposed V
+// copy stores each 16 keys in the order those registers hold them, so both
+// MFMA operands are plain 16-byte LDS reads.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "tile.hpp"
 
 namespace bwattn {
 
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void attn_fwd_kernel(FwdArgs a) {
-  constexpr int BQ = kFwdBlockQ, BK = kFwdBlockK, QG = 2;
+template <int D, int NW, int QG>
+__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
+  constexpr int NT = NW * 64;
+  constexpr int BQ = kFwdBlockQ, BK = kFwdBlockK;
+  static_assert(BQ == NW * 32 * QG, "query rows per workgroup");
   constexpr int NDC = D / 16;             // 16-wide k steps over D for S^T
   constexpr int NDG = D / 32;             // 32-row groups of O^T over D
   constexpr int TB = BK * D * 2;          // bytes per tile
   constexpr float kLazy = 8.f;
   using T = Tile<D>;
-  __shared__ __attribute__((aligned(16))) char smem[4 * TB];  // [buffer][K, V]
+  using TV = Tile<BK>;
+  __shared__ __attribute__((aligned(16))) char smem[4 * TB];  // [buffer][K, V^T]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hl = lane >> 5, l32 = lane & 31;
@@ -41,8 +44,9 @@ void attn_fwd_kernel(FwdArgs a) {
   const int S = a.S;
   const int64_t base = (int64_t)bh * S * D;
   const int Q0 = qt * BQ;
-  const int q0 = Q0 + w * 64;
-  const int qlast = min(S - 1, q0 + 63);
+  constexpr int QW = 32 * QG;  // rows per wave
+  const int q0 = Q0 + w * QW;
+  const int qlast = min(S - 1, q0 + QW - 1);
   const bool use_seg = a.seg != nullptr;
   const int32_t* segb = use_seg ? a.seg + (int64_t)b * S : nullptr;
   const int2* blkb = use_seg ? a.blk + (int64_t)b * a.nblk : nullptr;
@@ -63,7 +67,7 @@ void attn_fwd_kernel(FwdArgs a) {
     segq[qg] = (use_seg && ok) ? segb[row] : 0;
   }
   int2 wrange = make_int2(0, 0);
-  if (use_seg && q0 < S) wrange = seg_range(blkb, a.nblk, q0, min(64, S - q0));
+  if (use_seg && q0 < S) wrange = seg_range(blkb, a.nblk, q0, min(QW, S - q0));
 
   // K/V tile range and walk
   TileWalk walk;
@@ -96,11 +100,11 @@ void attn_fwd_kernel(FwdArgs a) {
   }
   const float sl2 = a.scale_log2;
   const uint16_t* kh = a.k + base;
-  const uint16_t* vh = a.v + base;
+  const uint16_t* vth = a.vt + (int64_t)bh * D * a.sp;
 
   if (walk.t >= 0) {
-    tile_to_lds<D, 256>(kh, walk.t * BK, S, smem, tid);
-    tile_to_lds<D, 256>(vh, walk.t * BK, S, smem + TB, tid);
+    tile_to_lds<D, NT>(kh, walk.t * BK, S, smem, tid);
+    tile_t_to_lds<D, NT>(vth, a.sp, walk.t * BK, smem + TB, tid);
   }
   wait_loads();
   __syncthreads();
@@ -110,8 +114,8 @@ void attn_fwd_kernel(FwdArgs a) {
     nx.next();
     if (nx.t >= 0) {
       char* nb = smem + (buf ^ 1) * 2 * TB;
-      tile_to_lds<D, 256>(kh, nx.t * BK, S, nb, tid);
-      tile_to_lds<D, 256>(vh, nx.t * BK, S, nb + TB, tid);
+      tile_to_lds<D, NT>(kh, nx.t * BK, S, nb, tid);
+      tile_t_to_lds<D, NT>(vth, a.sp, nx.t * BK, nb + TB, tid);
     }
 
     const int k0 = walk.t * BK;
@@ -145,7 +149,7 @@ void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             int j = k0 + 32 * kg + 8 * (r >> 2) + 4 * hl + (r & 3);
-            int sk = (seg_mask && j < S) ? segb[j] : 0;
+            int sk = seg_mask ? segb[min(j, S - 1)] : 0;
 #pragma unroll
             for (int qg = 0; qg < QG; ++qg) {
               int i = q0 + 32 * qg + l32;
@@ -200,7 +204,7 @@ void attn_fwd_kernel(FwdArgs a) {
         for (int c = 0; c < 2; ++c) {
 #pragma unroll
           for (int dg = 0; dg < NDG; ++dg) {
-            bf16x8 va = T::read_cols(vt, 32 * kg + 16 * c, 32 * dg, lane);
+            bf16x8 va = TV::read_rows(vt, 32 * dg, 2 * kg + c, lane);
 #pragma unroll
             for (int qg = 0; qg < QG; ++qg) o[qg][dg] = mfma32(va, pk[qg][c], o[qg][dg]);
           }
@@ -236,11 +240,12 @@ void attn_fwd_kernel(FwdArgs a) {
 }
 
 hipError_t launch_attn_fwd(const FwdArgs& a, int D, hipStream_t st) {
-  dim3 grid((unsigned)((int64_t)a.B * a.H * a.n_qtiles)), block(256);
+  constexpr int NW = 8, QG = 1;
+  dim3 grid((unsigned)((int64_t)a.B * a.H * a.n_qtiles)), block(NW * 64);
   if (D == 128)
-    hipLaunchKernelGGL(attn_fwd_kernel<128>, grid, block, 0, st, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<128, NW, QG>), grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL(attn_fwd_kernel<64>, grid, block, 0, st, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<64, NW, QG>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 

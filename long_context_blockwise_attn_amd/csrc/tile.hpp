@@ -67,6 +67,24 @@ __device__ __forceinline__ void tile_to_lds(const uint16_t* src, int r0, int S, 
   }
 }
 
+// Copy columns [c0, c0 + 64) of a transposed [D, sp] bf16 matrix (rows d,
+// sp a multiple of 64) into an LDS tile of D rows x 64 elements (Tile<64>
+// layout), by direct global-to-LDS loads.
+template <int D, int NT>
+__device__ __forceinline__ void tile_t_to_lds(const uint16_t* src, int sp, int c0, char* tile, int tid) {
+  constexpr int PER = D * 8 / NT;  // loads per wave (8 chunks per row of 64)
+  const int w = tid >> 6, lane = tid & 63;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    int blk = w * PER + i;
+    int p = blk * 64 + lane;
+    int row = p >> 3, phys = p & 7;
+    int logical = phys ^ Tile<64>::swz(row);
+    __builtin_amdgcn_global_load_lds((const void*)(src + (int64_t)row * sp + c0 + logical * 8),
+                                     (__attribute__((address_space(3))) void*)(tile + blk * 1024), 16, 0, 0);
+  }
+}
+
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0); }
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
