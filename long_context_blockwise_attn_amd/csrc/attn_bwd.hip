@@ -16,6 +16,9 @@
 //    tile pair (S, dP, dQ).
 //  - dK/dV kernel: a workgroup owns kBwdBlockK keys and streams Q/dO tiles of
 //    64 rows.  4 contractions per tile pair (S, dP, dV, dK).
+// Operands with k along the sequence (K^T for dQ, Q^T and dO^T for dK/dV)
+// come from transposed copies made by a pre-pass, so every MFMA operand is a
+// 16-byte LDS read.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "tile.hpp"
@@ -56,19 +59,21 @@ __device__ __forceinline__ void store_rows(uint16_t* dst_row, const f32x16 (&x)[
 }
 
 // ---------------------------------------------------------------------------
-// dQ (and Delta): 4 waves x 64 query rows; K/V tiles of 64 keys in LDS.
-// Per 32-key half: S^T = K Q^T and dP^T = V dO^T (lane = query row), then
-// dS^T = P^T (dP^T - Delta) and dQ^T += K^T dS^T with K^T from the
-// transposing LDS read.
+// dQ (and Delta): NW waves x 32 query rows; tiles of 64 keys of K, V and the
+// transposed K in LDS.  Per 32-key half: S^T = K Q^T and dP^T = V dO^T
+// (lane = query row), then dS^T = P^T (dP^T - Delta) and dQ^T += K^T dS^T.
 // ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void attn_bwd_dq_kernel(BwdArgs a) {
-  constexpr int BQ = kFwdBlockQ, BK = kFwdBlockK, QG = 2;
+template <int D, int NW, int NSTAGE>
+__global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
+  constexpr int BQ = kFwdBlockQ, BK = kFwdBlockK;
+  static_assert(BQ == NW * 32, "one 32-row group per wave");
   constexpr int NDC = D / 16, NDG = D / 32;
-  constexpr int TB = BK * D * 2;
-  using T = Tile<D>;
-  __shared__ __attribute__((aligned(16))) char smem[4 * TB];  // [buffer][K, V]
+  using KT = PTile<BK, D / 8>;   // K and V rows
+  using KTT = PTile<D, BK / 8>;  // K^T rows (d), 64 keys each
+  constexpr int SEG_OFF = 2 * KT::kBytes + KTT::kBytes;  // segment ids of the tile's keys
+  constexpr int BUF = SEG_OFF + 256;
+  // ring of [K, V, K^T, seg] stages (see run_pipeline)
+  __shared__ __attribute__((aligned(16))) char smem[NSTAGE * BUF];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hl = lane >> 5, l32 = lane & 31;
@@ -79,19 +84,16 @@ void attn_bwd_dq_kernel(BwdArgs a) {
   const int S = a.S;
   const int64_t base = (int64_t)bh * S * D;
   const int Q0 = qt * BQ;
-  const int q0 = Q0 + w * 64;
-  const int qlast = min(S - 1, q0 + 63);
+  const int q0 = Q0 + w * 32;
+  const int row = q0 + l32;  // this lane's query row
+  const bool ok = row < S;
   const bool use_seg = a.seg != nullptr;
   const int32_t* segb = use_seg ? a.seg + (int64_t)b * S : nullptr;
   const int2* blkb = use_seg ? a.blk + (int64_t)b * a.nblk : nullptr;
 
-  bf16x8 qop[QG][NDC], dop[QG][NDC];
-  int segq[QG];
-  float nlse2[QG], delta[QG];
-#pragma unroll
-  for (int qg = 0; qg < QG; ++qg) {
-    int row = q0 + 32 * qg + l32;
-    bool ok = row < S;
+  bf16x8 qop[NDC], dop[NDC];
+  float delta;
+  {
     int64_t ro = base + (int64_t)min(row, S - 1) * D + 8 * hl;
     float dsum = 0.f;
 #pragma unroll
@@ -99,20 +101,20 @@ void attn_bwd_dq_kernel(BwdArgs a) {
       bf16x8 qv = *(const bf16x8*)(a.q + ro + 16 * dc);
       u32x4 dv = *(const u32x4*)(a.dout + ro + 16 * dc);
       u32x4 ov = *(const u32x4*)(a.o + ro + 16 * dc);
-      qop[qg][dc] = ok ? qv : bf16x8{};
-      dop[qg][dc] = ok ? __builtin_bit_cast(bf16x8, dv) : bf16x8{};
+      qop[dc] = ok ? qv : bf16x8{};
+      dop[dc] = ok ? __builtin_bit_cast(bf16x8, dv) : bf16x8{};
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        dsum += bf16_lo(dv[e]) * bf16_lo(ov[e]) + bf16_hi(dv[e]) * bf16_hi(ov[e]);
+      for (int e = 0; e < 4; ++e) dsum += bf16_lo(dv[e]) * bf16_lo(ov[e]) + bf16_hi(dv[e]) * bf16_hi(ov[e]);
     }
     dsum = pair_sum(dsum);
-    delta[qg] = ok ? dsum : 0.f;
+    delta = ok ? dsum : 0.f;
     if (ok && hl == 0) a.delta[(int64_t)bh * S + row] = dsum;
-    nlse2[qg] = ok ? -a.lse[(int64_t)bh * S + row] * kLog2e : 0.f;
-    segq[qg] = (use_seg && ok) ? segb[row] : 0;
   }
+  const float nlse2 = ok ? -a.lse[(int64_t)bh * S + row] * kLog2e : 0.f;
+  const int segq = (use_seg && ok) ? segb[row] : 0;
+  const int qlast = min(S - 1, q0 + 31);
   int2 wrange = make_int2(0, 0);
-  if (use_seg && q0 < S) wrange = seg_range(blkb, a.nblk, q0, min(64, S - q0));
+  if (use_seg && q0 < S) wrange = seg_range(blkb, a.nblk, q0, min(32, S - q0));
 
   TileWalk walk;
   if (a.qrange) {
@@ -127,37 +129,34 @@ void attn_bwd_dq_kernel(BwdArgs a) {
   walk.nc = a.chunk_tiles ? (a.n_ktiles + a.chunk_tiles - 1) / a.chunk_tiles : 1;
   walk.r = a.chunk_tiles ? (Q0 / BK) / a.chunk_tiles : 0;
   walk.dir = -1;
+  walk.desc = false;
   walk.blk = blkb;
   walk.nblk = a.nblk;
   walk.rows = BK;
   walk.own = use_seg ? seg_range(blkb, a.nblk, Q0, min(BQ, S - Q0)) : make_int2(0, 0);
   walk.start();
 
-  f32x16 dq[QG][NDG];
+  f32x16 dq[NDG];
 #pragma unroll
-  for (int qg = 0; qg < QG; ++qg)
-#pragma unroll
-    for (int dg = 0; dg < NDG; ++dg) dq[qg][dg] = f32x16{};
+  for (int dg = 0; dg < NDG; ++dg) dq[dg] = f32x16{};
   const float sl2 = a.scale_log2;
   const uint16_t* kh = a.k + base;
   const uint16_t* vh = a.v + base;
-
-  if (walk.t >= 0) {
-    tile_to_lds<D, 256>(kh, walk.t * BK, S, smem, tid);
-    tile_to_lds<D, 256>(vh, walk.t * BK, S, smem + TB, tid);
-  }
-  wait_loads();
-  __syncthreads();
-  int buf = 0;
-  while (walk.t >= 0) {
-    TileWalk nx = walk;
-    nx.next();
-    if (nx.t >= 0) {
-      char* nb = smem + (buf ^ 1) * 2 * TB;
-      tile_to_lds<D, 256>(kh, nx.t * BK, S, nb, tid);
-      tile_to_lds<D, 256>(vh, nx.t * BK, S, nb + TB, tid);
-    }
-    const int k0 = walk.t * BK;
+  const uint16_t* kth = a.kt + (int64_t)bh * D * a.sp;
+  TileFill<BK, D / 8, NW> rfill;  // K and V rows
+  TileFill<D, BK / 8, NW> tfill;  // K^T rows
+  rfill.init(D * 2, tid);
+  tfill.init(a.sp * 2, tid);
+  auto load = [&](int t, char* buf) {
+    const uint32_t rbytes = (uint32_t)(S - t * BK) * D * 2;
+    rfill.fill(kh + (int64_t)t * BK * D, rbytes, buf);
+    rfill.fill(vh + (int64_t)t * BK * D, rbytes, buf + KT::kBytes);
+    tfill.fill(kth + t * BK, (uint32_t)(D * a.sp - t * BK) * 2, buf + 2 * KT::kBytes);
+    if (use_seg && w == 0) row64_to_lds(segb, t * BK, S, buf + SEG_OFF, lane);
+  };
+  const int per_tile = 2 * rfill.count() + tfill.count() + (use_seg && w == 0 ? 1 : 0);
+  auto compute = [&](int t, const char* buf) {
+    const int k0 = t * BK;
     bool skip = q0 >= S || (a.causal && k0 > qlast);
     bool seg_mask = false;
     if (use_seg && !skip) {
@@ -168,122 +167,100 @@ void attn_bwd_dq_kernel(BwdArgs a) {
         seg_mask = !(kr.x == kr.y && wrange.x == wrange.y && kr.x == wrange.x);
     }
     if (!skip) {
-      const char* kt = smem + buf * 2 * TB;
-      const char* vt = kt + TB;
+      const char* ktl = buf;
+      const char* vtl = buf + KT::kBytes;
+      const char* kttl = buf + 2 * KT::kBytes;
+      const int* segk_lds = (const int*)(buf + SEG_OFF);
       const bool need_mask = seg_mask || (k0 + BK > S) || (a.causal && k0 + BK - 1 > q0);
 #pragma unroll
       for (int kg = 0; kg < 2; ++kg) {
-        f32x16 s[QG], dp[QG];
-#pragma unroll
-        for (int qg = 0; qg < QG; ++qg) s[qg] = dp[qg] = f32x16{};
+        f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int dc = 0; dc < NDC; ++dc) {
-          bf16x8 ka = T::read_rows(kt, 32 * kg, dc, lane);
-          bf16x8 va = T::read_rows(vt, 32 * kg, dc, lane);
-#pragma unroll
-          for (int qg = 0; qg < QG; ++qg) {
-            s[qg] = mfma32(ka, qop[qg][dc], s[qg]);
-            dp[qg] = mfma32(va, dop[qg][dc], dp[qg]);
-          }
+          bf16x8 ka = KT::read(ktl, 32 * kg, dc, lane);
+          bf16x8 va = KT::read(vtl, 32 * kg, dc, lane);
+          s = mfma32(ka, qop[dc], s);
+          dp = mfma32(va, dop[dc], dp);
         }
         if (need_mask) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             int j = k0 + 32 * kg + 8 * (r >> 2) + 4 * hl + (r & 3);
-            int sk = (seg_mask && j < S) ? segb[j] : 0;
-#pragma unroll
-            for (int qg = 0; qg < QG; ++qg) {
-              int i = q0 + 32 * qg + l32;
-              bool vis = j < S && (!a.causal || j <= i) && (!seg_mask || sk == segq[qg]);
-              s[qg][r] = vis ? s[qg][r] : kNegInf;
-            }
+            int sk = 0;
+            if (use_seg) sk = segk_lds[j - k0];
+            bool vis = j < S && (!a.causal || j <= row) && (!use_seg || sk == segq);
+            s[r] = vis ? s[r] : kNegInf;
           }
         }
-        bf16x8 dsk[QG][2];
+        bf16x8 dsk[2];
 #pragma unroll
-        for (int qg = 0; qg < QG; ++qg) {
+        for (int r = 0; r < 16; ++r) {
+          float p = fast_exp2(__builtin_fmaf(s[r], sl2, nlse2));
+          s[r] = p * (dp[r] - delta);
+        }
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float p = fast_exp2(__builtin_fmaf(s[qg][r], sl2, nlse2[qg]));
-            s[qg][r] = p * (dp[qg][r] - delta[qg]);
-          }
-#pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            int r0 = 8 * c;
-            uint32_t w0 = pack_bf16x2(s[qg][r0 + 0], s[qg][r0 + 1]);
-            uint32_t w1 = pack_bf16x2(s[qg][r0 + 2], s[qg][r0 + 3]);
-            uint32_t w2 = pack_bf16x2(s[qg][r0 + 4], s[qg][r0 + 5]);
-            uint32_t w3 = pack_bf16x2(s[qg][r0 + 6], s[qg][r0 + 7]);
-            dsk[qg][c] = __builtin_bit_cast(bf16x8, u32x4{w0, w1, w2, w3});
-          }
+        for (int c = 0; c < 2; ++c) {
+          int r0 = 8 * c;
+          dsk[c] = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(s[r0], s[r0 + 1]), pack_bf16x2(s[r0 + 2], s[r0 + 3]),
+                                                    pack_bf16x2(s[r0 + 4], s[r0 + 5]), pack_bf16x2(s[r0 + 6], s[r0 + 7])});
         }
         // dQ^T += K^T dS^T over the 32 keys of this half
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
 #pragma unroll
           for (int dg = 0; dg < NDG; ++dg) {
-            bf16x8 kta = T::read_cols(kt, 32 * kg + 16 * c, 32 * dg, lane);
-#pragma unroll
-            for (int qg = 0; qg < QG; ++qg) dq[qg][dg] = mfma32(kta, dsk[qg][c], dq[qg][dg]);
+            bf16x8 kta = KTT::read(kttl, 32 * dg, 2 * kg + c, lane);
+            dq[dg] = mfma32(kta, dsk[c], dq[dg]);
           }
         }
       }
     }
-    wait_loads();
-    __syncthreads();
-    buf ^= 1;
-    walk = nx;
-  }
+  };
+  run_pipeline<NSTAGE>(walk, per_tile, smem, BUF, load, compute);
 
-#pragma unroll
-  for (int qg = 0; qg < QG; ++qg) {
-    int row = q0 + 32 * qg + l32;
-    if (row < S) {
-      if (a.rope) {
-        double pos = a.pos ? (double)a.pos[(int64_t)b * S + row] : (double)row;
-        rope_backward_row<NDG>(dq[qg], pos, a.turns, hl);
-      }
-      store_rows<D>(a.dq + base + (int64_t)row * D, dq[qg], a.scale, hl);
+  if (ok) {
+    if (a.rope) {
+      double pos = a.pos ? (double)a.pos[(int64_t)b * S + row] : (double)row;
+      rope_backward_row<NDG>(dq, pos, a.turns, hl);
     }
+    store_rows<D>(a.dq + base + (int64_t)row * D, dq, a.scale, hl);
   }
 }
 
 // ---------------------------------------------------------------------------
-// dK/dV: NW waves x 32 keys; Q/dO tiles of 64 rows in LDS.  Scores are kept
-// with lane = key: S = Q K^T and dP = dO V^T (K and V rows of the wave stay
-// in registers), then dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T
-// from the transposing LDS read.
+// dK/dV: NW waves x 32 keys; tiles of 64 query rows of Q, dO and their
+// transposed copies in LDS.  Scores are kept with lane = key: S = Q K^T and
+// dP = dO V^T (K and V rows of the lane's key stay in registers), then
+// dV^T += dO^T P and dK^T += Q^T dS.
 // ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void attn_bwd_dkdv_kernel(BwdArgs a) {
-  constexpr int NW = 4, BKV = kBwdBlockK, BQT = kBwdBlockQ;
+template <int D, int NW, int NSTAGE>
+__global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int BKV = kBwdBlockK, BQT = kBwdBlockQ;
   static_assert(BKV == NW * 32, "one 32-key group per wave");
   constexpr int NDC = D / 16, NDG = D / 32;
-  constexpr int TB = BQT * D * 2;
-  constexpr int SB = 4 * TB;         // row statistics after the four tiles
-  using T = Tile<D>;
-  // [buffer][Q, dO] tiles, then per buffer: LSE[64], Delta[64], seg[64]
-  __shared__ __attribute__((aligned(16))) char smem[4 * TB + 2 * 3 * 256];
+  using QT = PTile<BQT, D / 8>;   // Q and dO rows
+  using QTT = PTile<D, BQT / 8>;  // Q^T and dO^T rows (d), 64 query rows each
+  constexpr int SB = 2 * QT::kBytes + 2 * QTT::kBytes;  // row statistics: LSE[64], Delta[64], seg[64]
+  constexpr int BUF = SB + 3 * 256;
+  // ring of [Q, dO, Q^T, dO^T, statistics] stages (see run_pipeline)
+  __shared__ __attribute__((aligned(16))) char smem[NSTAGE * BUF];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hl = lane >> 5, l32 = lane & 31;
   int bh, rank;
   xcd_tile_order(blockIdx.x, a.B * a.H, a.n_bkv, bh, rank);
-  // causal work shrinks with the key tile index: low tiles first
-  const int kt_idx = rank;
+  const int kt_idx = rank;  // causal work shrinks with the key tile index: low tiles first
   const int b = bh / a.H;
   const int S = a.S;
   const int64_t base = (int64_t)bh * S * D;
   const int K0 = kt_idx * BKV;
-  const int j0 = K0 + 32 * w;         // this wave's first key
-  const int j = j0 + l32;             // this lane's key
+  const int j0 = K0 + 32 * w;  // this wave's first key
+  const int j = j0 + l32;      // this lane's key
   const bool jok = j < S;
   const bool use_seg = a.seg != nullptr;
   const int32_t* segb = use_seg ? a.seg + (int64_t)b * S : nullptr;
   const int2* blkb = use_seg ? a.blk + (int64_t)b * a.nblk : nullptr;
 
-  // K and V rows of this lane's key as B operands (k along d)
   bf16x8 kop[NDC], vop[NDC];
   {
     int64_t ro = base + (int64_t)min(j, S - 1) * D + 8 * hl;
@@ -312,6 +289,9 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
   walk.nc = a.chunk_tiles ? (a.n_bq + a.chunk_tiles - 1) / a.chunk_tiles : 1;
   walk.r = a.chunk_tiles ? (K0 / BQT) / a.chunk_tiles : 0;
   walk.dir = +1;
+  // natural order: from the last query tile down, so that workgroups of one
+  // head stream the same Q/dO tiles at the same time (L2 reuse)
+  walk.desc = true;
   walk.blk = blkb;
   walk.nblk = a.nblk;
   walk.rows = BQT;
@@ -324,40 +304,33 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
   const float sl2 = a.scale_log2;
   const uint16_t* qh = a.q + base;
   const uint16_t* dh = a.dout + base;
+  const uint16_t* qth = a.qt + (int64_t)bh * D * a.sp;
+  const uint16_t* dth = a.dot + (int64_t)bh * D * a.sp;
   const float* lse_h = a.lse + (int64_t)bh * S;
   const float* del_h = a.delta + (int64_t)bh * S;
 
-  // row statistics of a Q tile (LSE, Delta, segment id of its 64 rows),
-  // fetched by wave 0 straight into LDS
-  auto load_stats = [&](int t, int bsel) {
+  // tiles of a Q block and its row statistics (LSE, Delta, segment id),
+  // the statistics fetched by wave 0
+  TileFill<BQT, D / 8, NW> rfill;  // Q and dO rows
+  TileFill<D, BQT / 8, NW> tfill;  // Q^T and dO^T rows
+  rfill.init(D * 2, tid);
+  tfill.init(a.sp * 2, tid);
+  auto load = [&](int t, char* buf) {
+    const uint32_t rbytes = (uint32_t)(S - t * BQT) * D * 2;
+    const uint32_t tbytes = (uint32_t)(D * a.sp - t * BQT) * 2;
+    rfill.fill(qh + (int64_t)t * BQT * D, rbytes, buf);
+    rfill.fill(dh + (int64_t)t * BQT * D, rbytes, buf + QT::kBytes);
+    tfill.fill(qth + t * BQT, tbytes, buf + 2 * QT::kBytes);
+    tfill.fill(dth + t * BQT, tbytes, buf + 2 * QT::kBytes + QTT::kBytes);
     if (w == 0) {
-      int i = min(t * BQT + lane, S - 1);
-      char* st = smem + SB + bsel * 768;
-      __builtin_amdgcn_global_load_lds((const void*)(lse_h + i), (__attribute__((address_space(3))) void*)(st), 4, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(del_h + i), (__attribute__((address_space(3))) void*)(st + 256), 4, 0, 0);
-      if (use_seg)
-        __builtin_amdgcn_global_load_lds((const void*)(segb + i), (__attribute__((address_space(3))) void*)(st + 512), 4, 0, 0);
+      row64_to_lds(lse_h, t * BQT, S, buf + SB, lane);
+      row64_to_lds(del_h, t * BQT, S, buf + SB + 256, lane);
+      if (use_seg) row64_to_lds(segb, t * BQT, S, buf + SB + 512, lane);
     }
   };
-
-  if (walk.t >= 0) {
-    tile_to_lds<D, 256>(qh, walk.t * BQT, S, smem, tid);
-    tile_to_lds<D, 256>(dh, walk.t * BQT, S, smem + TB, tid);
-    load_stats(walk.t, 0);
-  }
-  wait_loads();
-  __syncthreads();
-  int buf = 0;
-  while (walk.t >= 0) {
-    TileWalk nx = walk;
-    nx.next();
-    if (nx.t >= 0) {
-      char* nb = smem + (buf ^ 1) * 2 * TB;
-      tile_to_lds<D, 256>(qh, nx.t * BQT, S, nb, tid);
-      tile_to_lds<D, 256>(dh, nx.t * BQT, S, nb + TB, tid);
-      load_stats(nx.t, buf ^ 1);
-    }
-    const int i0 = walk.t * BQT;
+  const int per_tile = 2 * rfill.count() + 2 * tfill.count() + (w == 0 ? (use_seg ? 3 : 2) : 0);
+  auto compute = [&](int t, const char* buf) {
+    const int i0 = t * BQT;
     const int ilast = min(S - 1, i0 + BQT - 1);
     bool skip = j0 >= S || (a.causal && ilast < j0);
     bool seg_mask = false;
@@ -369,27 +342,22 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
         seg_mask = !(qr.x == qr.y && wrange.x == wrange.y && qr.x == wrange.x);
     }
     if (!skip) {
-      const char* qtl = smem + buf * 2 * TB;
-      const char* dtl = qtl + TB;
-      const float* st = (const float*)(smem + SB + buf * 768);
+      const char* qtl = buf;
+      const char* dtl = buf + QT::kBytes;
+      const char* qttl = buf + 2 * QT::kBytes;
+      const char* dttl = buf + 2 * QT::kBytes + QTT::kBytes;
+      const float* st = (const float*)(buf + SB);
       const bool need_mask = seg_mask || (i0 + BQT > S) || (a.causal && i0 < j0 + 31);
 #pragma unroll
       for (int qg = 0; qg < 2; ++qg) {
-        // S[i][j] and dP[i][j] for 32 rows i = i0 + 32 qg + 8 (r/4) + 4 hl + r%4
+        // S[i][j] and dP[i][j] for rows i = i0 + 32 qg + 8 (r/4) + 4 hl + r%4
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int dc = 0; dc < NDC; ++dc) {
-          bf16x8 qa = T::read_rows(qtl, 32 * qg, dc, lane);
-          bf16x8 da = T::read_rows(dtl, 32 * qg, dc, lane);
+          bf16x8 qa = QT::read(qtl, 32 * qg, dc, lane);
+          bf16x8 da = QT::read(dtl, 32 * qg, dc, lane);
           s = mfma32(qa, kop[dc], s);
           dp = mfma32(da, vop[dc], dp);
-        }
-        f32x4 nl[4], de[4];
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          int ri = 32 * qg + 8 * rq + 4 * hl;
-          nl[rq] = *(const f32x4*)(st + ri) * -kLog2e;
-          de[rq] = *(const f32x4*)(st + 64 + ri);
         }
         if (need_mask) {
 #pragma unroll
@@ -397,44 +365,51 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
             int ri = 32 * qg + 8 * (r >> 2) + 4 * hl + (r & 3);
             int i = i0 + ri;
             int sq = ((const int*)st)[128 + ri];
-            bool vis = i < S && (!a.causal || j <= i) && (!seg_mask || sq == segk);
+            bool vis = i < S && (!a.causal || j <= i) && (!use_seg || sq == segk);
             s[r] = vis ? s[r] : kNegInf;
           }
         }
+        // P = exp(S scale - LSE) and dS = P (dP - Delta); the statistics of
+        // each 4 rows are read from LDS where they are used
         bf16x8 pk[2], dsk[2];
-        float pv[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(__builtin_fmaf(s[r], sl2, nl[r >> 2][r & 3]));
-          pv[r] = p;
-          s[r] = p * (dp[r] - de[r >> 2][r & 3]);
-        }
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          int r0 = 8 * c;
-          pk[c] = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(pv[r0], pv[r0 + 1]), pack_bf16x2(pv[r0 + 2], pv[r0 + 3]),
-                                                   pack_bf16x2(pv[r0 + 4], pv[r0 + 5]), pack_bf16x2(pv[r0 + 6], pv[r0 + 7])});
-          dsk[c] = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(s[r0], s[r0 + 1]), pack_bf16x2(s[r0 + 2], s[r0 + 3]),
-                                                    pack_bf16x2(s[r0 + 4], s[r0 + 5]), pack_bf16x2(s[r0 + 6], s[r0 + 7])});
+          uint32_t pw[4], dw[4];
+#pragma unroll
+          for (int hq = 0; hq < 2; ++hq) {
+            const int rq = 2 * c + hq;
+            const int ri = 32 * qg + 8 * rq + 4 * hl;
+            const f32x4 nl = *(const f32x4*)(st + ri) * -kLog2e;
+            const f32x4 de = *(const f32x4*)(st + 64 + ri);
+            float pv[4], dsv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              pv[e] = fast_exp2(__builtin_fmaf(s[4 * rq + e], sl2, nl[e]));
+              dsv[e] = pv[e] * (dp[4 * rq + e] - de[e]);
+            }
+            pw[2 * hq] = pack_bf16x2(pv[0], pv[1]);
+            pw[2 * hq + 1] = pack_bf16x2(pv[2], pv[3]);
+            dw[2 * hq] = pack_bf16x2(dsv[0], dsv[1]);
+            dw[2 * hq + 1] = pack_bf16x2(dsv[2], dsv[3]);
+          }
+          pk[c] = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+          dsk[c] = __builtin_bit_cast(bf16x8, u32x4{dw[0], dw[1], dw[2], dw[3]});
         }
         // dV^T += dO^T P, dK^T += Q^T dS over these 32 rows
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
 #pragma unroll
           for (int dg = 0; dg < NDG; ++dg) {
-            bf16x8 dta = T::read_cols(dtl, 32 * qg + 16 * c, 32 * dg, lane);
-            bf16x8 qta = T::read_cols(qtl, 32 * qg + 16 * c, 32 * dg, lane);
+            bf16x8 dta = QTT::read(dttl, 32 * dg, 2 * qg + c, lane);
+            bf16x8 qta = QTT::read(qttl, 32 * dg, 2 * qg + c, lane);
             dv[dg] = mfma32(dta, pk[c], dv[dg]);
             dk[dg] = mfma32(qta, dsk[c], dk[dg]);
           }
         }
       }
     }
-    wait_loads();
-    __syncthreads();
-    buf ^= 1;
-    walk = nx;
-  }
+  };
+  run_pipeline<NSTAGE>(walk, per_tile, smem, BUF, load, compute);
 
   if (jok) {
     if (a.rope) {
@@ -447,20 +422,22 @@ void attn_bwd_dkdv_kernel(BwdArgs a) {
 }
 
 hipError_t launch_attn_bwd_dq(const BwdArgs& a, int D, hipStream_t st) {
-  dim3 grid((unsigned)((int64_t)a.B * a.H * a.n_qtiles)), block(256);
+  constexpr int NW = 8, NSTAGE = 2;
+  dim3 grid((unsigned)((int64_t)a.B * a.H * a.n_qtiles)), block(NW * 64);
   if (D == 128)
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, grid, block, 0, st, a);
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<128, NW, NSTAGE>), grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, grid, block, 0, st, a);
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<64, NW, NSTAGE>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_bwd_dkdv(const BwdArgs& a, int D, hipStream_t st) {
-  dim3 grid((unsigned)((int64_t)a.B * a.H * a.n_bkv)), block(256);
+  constexpr int NW = 8, NSTAGE = 2;
+  dim3 grid((unsigned)((int64_t)a.B * a.H * a.n_bkv)), block(NW * 64);
   if (D == 128)
-    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<128>, grid, block, 0, st, a);
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<128, NW, NSTAGE>), grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<64>, grid, block, 0, st, a);
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<64, NW, NSTAGE>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 

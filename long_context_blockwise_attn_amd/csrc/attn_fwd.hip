@@ -22,18 +22,21 @@
 
 namespace bwattn {
 
-template <int D, int NW, int QG>
+template <int D, int NW, int QG, int NSTAGE>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
-  constexpr int NT = NW * 64;
   constexpr int BQ = kFwdBlockQ, BK = kFwdBlockK;
   static_assert(BQ == NW * 32 * QG, "query rows per workgroup");
+  static_assert(BK == 64, "two 32-key halves per tile");
   constexpr int NDC = D / 16;             // 16-wide k steps over D for S^T
   constexpr int NDG = D / 32;             // 32-row groups of O^T over D
-  constexpr int TB = BK * D * 2;          // bytes per tile
   constexpr float kLazy = 8.f;
-  using T = Tile<D>;
-  using TV = Tile<BK>;
-  __shared__ __attribute__((aligned(16))) char smem[4 * TB];  // [buffer][K, V^T]
+  using KT = PTile<BK, D / 8>;            // K rows
+  using VT = PTile<D, BK / 8>;            // V^T rows (d), 64 keys each
+  constexpr int SEG_OFF = KT::kBytes + VT::kBytes;  // segment ids of the tile's keys
+  constexpr int BUF = SEG_OFF + 256;
+  // NSTAGE-deep ring of [K, V^T, seg] tiles: the loads for tile
+  // t + NSTAGE - 1 are in flight while tile t is computed
+  __shared__ __attribute__((aligned(16))) char smem[NSTAGE * BUF];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hl = lane >> 5, l32 = lane & 31;
@@ -83,6 +86,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   walk.nc = a.chunk_tiles ? (a.n_ktiles + a.chunk_tiles - 1) / a.chunk_tiles : 1;
   walk.r = a.chunk_tiles ? (Q0 / BK) / a.chunk_tiles : 0;
   walk.dir = -1;
+  walk.desc = false;
   walk.blk = blkb;
   walk.nblk = a.nblk;
   walk.rows = BK;
@@ -101,24 +105,19 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   const float sl2 = a.scale_log2;
   const uint16_t* kh = a.k + base;
   const uint16_t* vth = a.vt + (int64_t)bh * D * a.sp;
-
-  if (walk.t >= 0) {
-    tile_to_lds<D, NT>(kh, walk.t * BK, S, smem, tid);
-    tile_t_to_lds<D, NT>(vth, a.sp, walk.t * BK, smem + TB, tid);
-  }
-  wait_loads();
-  __syncthreads();
-  int buf = 0;
-  while (walk.t >= 0) {
-    TileWalk nx = walk;
-    nx.next();
-    if (nx.t >= 0) {
-      char* nb = smem + (buf ^ 1) * 2 * TB;
-      tile_to_lds<D, NT>(kh, nx.t * BK, S, nb, tid);
-      tile_t_to_lds<D, NT>(vth, a.sp, nx.t * BK, nb + TB, tid);
-    }
-
-    const int k0 = walk.t * BK;
+  TileFill<BK, D / 8, NW> kfill;  // K rows
+  TileFill<D, BK / 8, NW> vfill;  // V^T rows
+  kfill.init(D * 2, tid);
+  vfill.init(a.sp * 2, tid);
+  auto load = [&](int t, char* buf) {
+    kfill.fill(kh + (int64_t)t * BK * D, (uint32_t)(S - t * BK) * D * 2, buf);
+    vfill.fill(vth + t * BK, (uint32_t)(D * a.sp - t * BK) * 2, buf + KT::kBytes);
+    if (use_seg && w == 0) row64_to_lds(segb, t * BK, S, buf + SEG_OFF, lane);
+  };
+  // vector-memory instructions this wave issues per tile
+  const int per_tile = kfill.count() + vfill.count() + (use_seg && w == 0 ? 1 : 0);
+  auto compute = [&](int t, const char* buf) {
+    const int k0 = t * BK;
     bool skip = q0 >= S || (a.causal && k0 > qlast);
     bool seg_mask = false;
     if (use_seg && !skip) {
@@ -129,35 +128,43 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
         seg_mask = !(kr.x == kr.y && wrange.x == wrange.y && kr.x == wrange.x);
     }
     if (!skip) {
-      const char* kt = smem + buf * 2 * TB;
-      const char* vt = kt + TB;
-      const bool need_mask = seg_mask || (k0 + BK > S) || (a.causal && k0 + BK - 1 > q0);
-      // two halves of 32 keys: scores, softmax merge, then P V for that half
+      const char* kt = buf;
+      const char* vt = buf + KT::kBytes;
+      const int* segk_lds = (const int*)(buf + SEG_OFF);
+      // S^T = K Q^T for both 32-key halves (independent accumulator chains):
+      // s[qg][kg] holds keys k0 + 32 kg + 8 (r/4) + 4 hl + r%4 of row l32
+      f32x16 s[QG][2];
 #pragma unroll
-      for (int kg = 0; kg < 2; ++kg) {
-        // S^T = K Q^T: s[qg] holds keys k0 + 32 kg + 8 (r/4) + 4 hl + r%4 of row l32
-        f32x16 s[QG];
+      for (int qg = 0; qg < QG; ++qg) s[qg][0] = s[qg][1] = f32x16{};
 #pragma unroll
-        for (int qg = 0; qg < QG; ++qg) s[qg] = f32x16{};
+      for (int dc = 0; dc < NDC; ++dc) {
 #pragma unroll
-        for (int dc = 0; dc < NDC; ++dc) {
-          bf16x8 ka = T::read_rows(kt, 32 * kg, dc, lane);
+        for (int kg = 0; kg < 2; ++kg) {
+          bf16x8 ka = KT::read(kt, 32 * kg, dc, lane);
 #pragma unroll
-          for (int qg = 0; qg < QG; ++qg) s[qg] = mfma32(ka, qop[qg][dc], s[qg]);
+          for (int qg = 0; qg < QG; ++qg) s[qg][kg] = mfma32(ka, qop[qg][dc], s[qg][kg]);
         }
-        if (need_mask) {
+      }
+      if (seg_mask || (k0 + BK > S) || (a.causal && k0 + BK - 1 > q0)) {
+        // partial tile: causal, segment and sequence-end masks
+        int jb = k0 + 4 * hl;
+#pragma unroll
+        for (int kg = 0; kg < 2; ++kg)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            int j = k0 + 32 * kg + 8 * (r >> 2) + 4 * hl + (r & 3);
-            int sk = seg_mask ? segb[min(j, S - 1)] : 0;
+            int j = jb + 32 * kg + 8 * (r >> 2) + (r & 3);
+            int sk = 0;
+            if (use_seg) sk = segk_lds[j - k0];
 #pragma unroll
             for (int qg = 0; qg < QG; ++qg) {
               int i = q0 + 32 * qg + l32;
-              bool vis = j < S && (!a.causal || j <= i) && (!seg_mask || sk == segq[qg]);
-              s[qg][r] = vis ? s[qg][r] : kNegInf;
+              bool vis = j < S && (!a.causal || j <= i) && (!use_seg || sk == segq[qg]);
+              s[qg][kg][r] = vis ? s[qg][kg][r] : kNegInf;
             }
           }
-        }
+      }
+#pragma unroll
+      for (int kg = 0; kg < 2; ++kg) {
         // Online softmax merge.  A row's running max m is raised only when
         // its new max exceeds it by more than kLazy (log2 units); otherwise
         // the stale m stays, p <= 2^kLazy, and O is not touched.  l and O
@@ -167,9 +174,11 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
         bf16x8 pk[QG][2];
 #pragma unroll
         for (int qg = 0; qg < QG; ++qg) {
-          float mx = kNegInf;
+          f32x16& sv = s[qg][kg];
+          float mx = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qg][r]);
+          for (int r = 3; r < 15; r += 2) mx = fmaxf(fmaxf(mx, sv[r]), sv[r + 1]);
+          mx = fmaxf(mx, sv[15]);
           mx = pair_max(mx) * sl2;
           const bool grow = mx > m[qg] + kLazy;
           if (__ballot(grow)) {
@@ -181,41 +190,35 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
             m[qg] = mnew;
           }
           const float muse = (m[qg] == kNegInf) ? 0.f : m[qg];
-          float rs = 0.f;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float p = fast_exp2(__builtin_fmaf(s[qg][r], sl2, -muse));
-            s[qg][r] = p;
-            rs += p;
-          }
-          lsum[qg] += rs;
+          for (int r = 0; r < 16; ++r) sv[r] = fast_exp2(__builtin_fmaf(sv[r], sl2, -muse));
+          // P in bf16 feeds the MFMA; the row sum adds the same bf16 values
+          float rs = lsum[qg];
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
             int r0 = 8 * c;
-            uint32_t w0 = pack_bf16x2(s[qg][r0 + 0], s[qg][r0 + 1]);
-            uint32_t w1 = pack_bf16x2(s[qg][r0 + 2], s[qg][r0 + 3]);
-            uint32_t w2 = pack_bf16x2(s[qg][r0 + 4], s[qg][r0 + 5]);
-            uint32_t w3 = pack_bf16x2(s[qg][r0 + 6], s[qg][r0 + 7]);
-            pk[qg][c] = __builtin_bit_cast(bf16x8, u32x4{w0, w1, w2, w3});
+            u32x4 pw = {pack_bf16x2(sv[r0], sv[r0 + 1]), pack_bf16x2(sv[r0 + 2], sv[r0 + 3]),
+                        pack_bf16x2(sv[r0 + 4], sv[r0 + 5]), pack_bf16x2(sv[r0 + 6], sv[r0 + 7])};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rs = dot2_bf16(pw[e], kBf16OnePair, rs);
+            pk[qg][c] = __builtin_bit_cast(bf16x8, pw);
           }
+          lsum[qg] = rs;
         }
         // O^T += V^T P^T over the 32 keys of this half
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
 #pragma unroll
           for (int dg = 0; dg < NDG; ++dg) {
-            bf16x8 va = TV::read_rows(vt, 32 * dg, 2 * kg + c, lane);
+            bf16x8 va = VT::read(vt, 32 * dg, 2 * kg + c, lane);
 #pragma unroll
             for (int qg = 0; qg < QG; ++qg) o[qg][dg] = mfma32(va, pk[qg][c], o[qg][dg]);
           }
         }
       }
     }
-    wait_loads();
-    __syncthreads();
-    buf ^= 1;
-    walk = nx;
-  }
+  };
+  run_pipeline<NSTAGE>(walk, per_tile, smem, BUF, load, compute);
 
   // epilogue: O = O^T / l, LSE = ln2 (m + log2 l)
 #pragma unroll
@@ -240,12 +243,12 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
 }
 
 hipError_t launch_attn_fwd(const FwdArgs& a, int D, hipStream_t st) {
-  constexpr int NW = 8, QG = 1;
+  constexpr int NW = 8, QG = 1, NSTAGE = 3;
   dim3 grid((unsigned)((int64_t)a.B * a.H * a.n_qtiles)), block(NW * 64);
   if (D == 128)
-    hipLaunchKernelGGL((attn_fwd_kernel<128, NW, QG>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<128, NW, QG, NSTAGE>), grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<64, NW, QG>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<64, NW, QG, NSTAGE>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 

@@ -8,7 +8,7 @@ namespace bwattn {
 // Tile sizes shared by the host schedule and the kernels.
 constexpr int kFwdBlockQ = 256;   // query rows per forward / dQ workgroup (4 waves x 64 rows)
 constexpr int kFwdBlockK = 64;    // keys per K/V tile streamed by the forward / dQ kernels
-constexpr int kBwdBlockK = 128;   // keys per dK/dV workgroup (4 waves x 32 keys)
+constexpr int kBwdBlockK = 256;   // keys per dK/dV workgroup (8 waves x 32 keys)
 constexpr int kBwdBlockQ = 64;    // query rows per Q/dO tile streamed by the dK/dV kernel
 constexpr int kSegBlock = 32;     // rows per segment-range block
 
@@ -64,6 +64,10 @@ struct BwdArgs {
   const uint16_t* q;   // rotated queries
   const uint16_t* k;   // rotated keys
   const uint16_t* v;
+  const uint16_t* qt;  // transposed copies [B,H,D,Sp] (order as TransposeArgs)
+  const uint16_t* kt;
+  const uint16_t* dot;
+  int sp;
   const uint16_t* o;
   const uint16_t* dout;
   const float* lse;    // natural log

@@ -5,87 +5,119 @@
 
 namespace bwattn {
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-// A tile of `rows` x D bf16 in LDS, row-major.  Each row's 16-byte chunks are
-// XOR-swizzled by swz(row) so that both operand reads below hit 32 distinct
-// banks per group of lanes: the 16-byte read (8 consecutive rows, one chunk)
-// and the transposing 8-byte read (4 consecutive rows, two adjacent chunks).
-template <int D>
-struct Tile {
-  static constexpr int kRowBytes = 2 * D;
-  static constexpr int kChunks = D / 8;
-  __device__ static __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
-  __device__ static __forceinline__ uint32_t off(int row, int chunk) {
-    return (uint32_t)(row * kRowBytes + ((chunk ^ swz(row)) << 4));
-  }
-  // MFMA operand whose lane l holds row r0 + (l % 32), columns
-  // 16 c + 8 (l / 32) + [0, 8): a 32x32x16 operand with k along the row.
-  __device__ static __forceinline__ bf16x8 read_rows(const char* t, int r0, int c, int lane) {
-    return *(const bf16x8*)(t + off(r0 + (lane & 31), 2 * c + (lane >> 5)));
-  }
-  // MFMA operand with k along the column: lane l holds column col0 + (l % 32)
-  // at rows r0 + 4h + {0..3} and r0 + 8 + 4h + {0..3} (h = l / 32), built
-  // from two transposing 8-byte reads (ds_read_b64_tr_b16: within a group of
-  // 16 lanes, output lane i element r comes from source lane 4r + i/4,
-  // element i % 4).
-  __device__ static __forceinline__ bf16x8 read_cols(const char* t, int r0, int col0, int lane) {
-    int j = lane & 15;
-    int col = col0 + ((lane >> 4) & 1) * 16 + 4 * (j & 3);
-    int row = r0 + 4 * (lane >> 5) + (j >> 2);
-    uint32_t sub = ((col >> 2) & 1) * 8;
-    const char* p1 = t + off(row, col >> 3) + sub;
-    const char* p2 = t + off(row + 8, col >> 3) + sub;
-    s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1));
-    s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p2));
-    typedef short s16x8 __attribute__((ext_vector_type(8)));
-    s16x8 r = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return __builtin_bit_cast(bf16x8, r);
+// An LDS tile of R rows x C 16-byte chunks (8 bf16 each), row-major with one
+// chunk of padding per row.  With a row stride of (C+1)*16 bytes, the 16-byte
+// reads of 16 consecutive rows at one chunk land on 16 distinct 16-byte bank
+// groups (64 banks of 4 bytes), and 8 consecutive rows on 8 distinct groups
+// of a 32-bank layout, so the MFMA operand reads below are conflict-free,
+// and a lane's reads at different chunks differ by immediate offsets.
+template <int R, int C>
+struct PTile {
+  static constexpr int kStride = (C + 1) * 16;
+  static constexpr int kBytes = R * kStride;
+  static constexpr int kBlocks = R * (C + 1) / 64;  // 1 KiB direct-load blocks
+  static_assert((R * (C + 1)) % 64 == 0, "tile must be whole 1 KiB blocks");
+  // MFMA operand whose lane l holds row r0 + (l % 32) at chunk
+  // 2 c + (l / 32): a 32x32x16 operand with k along the row.
+  __device__ static __forceinline__ bf16x8 read(const char* t, int r0, int c, int lane) {
+    return *(const bf16x8*)(t + (r0 + (lane & 31)) * kStride + (2 * c + (lane >> 5)) * 16);
   }
 };
 
-// Copy rows [r0, r0 + 64) of a [S, D] bf16 matrix into an LDS tile with the
-// swizzled layout, by direct global-to-LDS loads (no registers).  NT threads
-// share the copy; each 64-lane load fills 1 KiB of consecutive LDS, so lane
-// i of a load fetches the global chunk that belongs at its LDS position.
-// Rows at or past S read row S-1 instead (finite data that the kernels mask).
-template <int D, int NT>
-__device__ __forceinline__ void tile_to_lds(const uint16_t* src, int r0, int S, char* tile, int tid) {
-  constexpr int NCH = D / 8;
-  constexpr int PER = 64 * NCH / NT;  // loads per wave
-  const int w = tid >> 6, lane = tid & 63;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    int blk = w * PER + i;
-    int p = blk * 64 + lane;
-    int row = p / NCH, phys = p % NCH;
-    int logical = phys ^ Tile<D>::swz(row);
-    int key = min(r0 + row, S - 1);
-    __builtin_amdgcn_global_load_lds((const void*)(src + (int64_t)key * D + logical * 8),
-                                     (__attribute__((address_space(3))) void*)(tile + blk * 1024), 16, 0, 0);
-  }
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource over `bytes` bytes from `base` (stride 0): loads at
+// offsets past the end return zero.  Word 3 is the raw-buffer format word of
+// gfx9.  The value is uniform across the wave.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  uint64_t a = (uint64_t)base;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xffff);
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;
+  return r;
 }
 
-// Copy columns [c0, c0 + 64) of a transposed [D, sp] bf16 matrix (rows d,
-// sp a multiple of 64) into an LDS tile of D rows x 64 elements (Tile<64>
-// layout), by direct global-to-LDS loads.
-template <int D, int NT>
-__device__ __forceinline__ void tile_t_to_lds(const uint16_t* src, int sp, int c0, char* tile, int tid) {
-  constexpr int PER = D * 8 / NT;  // loads per wave (8 chunks per row of 64)
-  const int w = tid >> 6, lane = tid & 63;
+// Direct buffer-to-LDS loads: lane i writes its 16 (or 4) bytes at LDS byte
+// address lds + 16 i (4 i); lds is uniform across the wave.  Issued through
+// inline assembly so that the compiler does not treat the in-flight LDS write
+// as aliasing the LDS reads that follow: the kernels wait for these loads
+// themselves (wait_vmem_le + barrier) before reading the destination.  The
+// instructions have no register results.
+__device__ __forceinline__ void dma_b128(i32x4 rsrc, const char* lds, uint32_t voffset) {
+  uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voffset), "s"(rsrc)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma_b32(i32x4 rsrc, const char* lds, uint32_t voffset) {
+  uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(m0), "v"(voffset), "s"(rsrc)
+               : "memory", "m0");
+}
+
+// Direct buffer-to-LDS fill of a PTile<R, C>.  Each 64-lane load fills
+// 1 KiB of consecutive LDS, so lane i fetches the global chunk that belongs at
+// its LDS position (pad slots fetch a repeat of the row's last chunk).  The NW
+// waves share the kBlocks blocks; a wave's per-lane byte offsets depend only
+// on the lane and the row pitch, so they are formed once (init) and each tile
+// only moves the buffer base.
+template <int R, int C, int NW>
+struct TileFill {
+  static constexpr int kBlocks = PTile<R, C>::kBlocks;
+  static constexpr int kPer = (kBlocks + NW - 1) / NW;
+  uint32_t voff[kPer];
+  int w;
+  __device__ void init(uint32_t row_bytes, int tid) {
+    w = tid >> 6;
+    const int lane = tid & 63;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    int blk = w * PER + i;
-    int p = blk * 64 + lane;
-    int row = p >> 3, phys = p & 7;
-    int logical = phys ^ Tile<64>::swz(row);
-    __builtin_amdgcn_global_load_lds((const void*)(src + (int64_t)row * sp + c0 + logical * 8),
-                                     (__attribute__((address_space(3))) void*)(tile + blk * 1024), 16, 0, 0);
+    for (int i = 0; i < kPer; ++i) {
+      int p = (w + NW * i) * 64 + lane;
+      int row = p / (C + 1), c = min(p % (C + 1), C - 1);
+      voff[i] = row * row_bytes + c * 16;
+    }
   }
+  // number of load instructions this wave issues per fill
+  __device__ int count() const { return kBlocks / NW + (w < kBlocks % NW ? 1 : 0); }
+  // rows of the tile start at src; reads at or past `bytes` return zero
+  __device__ void fill(const void* src, uint32_t bytes, char* tile) const {
+    const i32x4 rs = make_rsrc(src, bytes);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      int blk = w + NW * i;
+      if (kBlocks % NW == 0 || blk < kBlocks) dma_b128(rs, tile + blk * 1024, voff[i]);
+    }
+  }
+};
+
+// 64 consecutive 4-byte values from src[i0 ..] into LDS (one wave; values
+// past `n` read as zero).
+__device__ __forceinline__ void row64_to_lds(const void* src, int i0, int n, char* dst, int lane) {
+  const i32x4 rs = make_rsrc((const char*)src + (int64_t)i0 * 4, (uint32_t)(n - i0) * 4);
+  dma_b32(rs, dst, lane * 4);
 }
 
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Wait until at most n vector-memory operations of this wave are in flight
+// (n uniform across the wave, 0 <= n < 64).  s_waitcnt takes an immediate,
+// hence the table; expcnt and lgkmcnt are left at their maxima.
+__device__ __forceinline__ void wait_vmem_le(int n) {
+#define BWATTN_VMCNT(k) \
+  case k: __builtin_amdgcn_s_waitcnt(((k) & 15) | (((k) >> 4) << 14) | 0x0F70); break;
+  switch (n) {
+    BWATTN_VMCNT(0) BWATTN_VMCNT(1) BWATTN_VMCNT(2) BWATTN_VMCNT(3) BWATTN_VMCNT(4) BWATTN_VMCNT(5)
+    BWATTN_VMCNT(6) BWATTN_VMCNT(7) BWATTN_VMCNT(8) BWATTN_VMCNT(9) BWATTN_VMCNT(10) BWATTN_VMCNT(11)
+    BWATTN_VMCNT(12) BWATTN_VMCNT(13) BWATTN_VMCNT(14) BWATTN_VMCNT(15) BWATTN_VMCNT(16) BWATTN_VMCNT(17)
+    BWATTN_VMCNT(18) BWATTN_VMCNT(19) BWATTN_VMCNT(20) BWATTN_VMCNT(21) BWATTN_VMCNT(22) BWATTN_VMCNT(23)
+    BWATTN_VMCNT(24) BWATTN_VMCNT(25) BWATTN_VMCNT(26) BWATTN_VMCNT(27) BWATTN_VMCNT(28) BWATTN_VMCNT(29)
+    BWATTN_VMCNT(30) BWATTN_VMCNT(31)
+    default: __builtin_amdgcn_s_waitcnt(0); break;
+  }
+#undef BWATTN_VMCNT
+}
+
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -105,7 +137,12 @@ __device__ __forceinline__ int2 range_union(int2 a, int2 b) { return make_int2(m
 __device__ __forceinline__ bool ranges_meet(int2 a, int2 b) { return !(a.y < b.x || a.x > b.y); }
 
 // Segment-id range of rows [r0, r0 + rows) from the 32-row block ranges.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// (r0 and rows are uniform across the wave; the loads are scalar.)
 __device__ __forceinline__ int2 seg_range(const int2* blk, int nblk, int r0, int rows) {
+  r0 = uniform(r0);
+  rows = uniform(rows);
   int b0 = r0 >> 5, b1 = min(nblk, (r0 + rows + 31) >> 5);
   int2 acc = blk[b0];
   for (int k = b0 + 1; k < b1; ++k) acc = range_union(acc, blk[k]);
@@ -122,6 +159,7 @@ __device__ __forceinline__ int2 seg_range(const int2* blk, int nblk, int r0, int
 // uniform across the workgroup.
 struct TileWalk {
   int lo, hi, ct, nc, r, dir;
+  bool desc;  // natural order (ct == 0) only: visit hi-1 down to lo
   int step, t;
   const int2* blk;
   int nblk, rows;
@@ -130,9 +168,19 @@ struct TileWalk {
     return blk == nullptr || ranges_meet(seg_range(blk, nblk, tile * rows, rows), own);
   }
   __device__ void seek(int after) {
+    if (ct == 0 && blk == nullptr) {  // natural order, every tile useful
+      int c = desc ? after - 1 : after + 1;
+      t = (c >= lo && c < hi) ? c : -1;
+      return;
+    }
     if (ct == 0) {
-      for (int c = after + 1; c < hi; ++c)
-        if (useful(c)) { t = c; return; }
+      if (desc) {
+        for (int c = after - 1; c >= lo; --c)
+          if (useful(c)) { t = c; return; }
+      } else {
+        for (int c = after + 1; c < hi; ++c)
+          if (useful(c)) { t = c; return; }
+      }
       t = -1;
       return;
     }
@@ -150,9 +198,51 @@ struct TileWalk {
   }
   __device__ void start() {
     step = 0;
-    seek(lo - 1);
+    seek(ct == 0 && desc ? hi : lo - 1);
   }
   __device__ void next() { seek(t); }
 };
+
+// Software pipeline over the tile walk with an NSTAGE ring of LDS buffers
+// (ring[i] = base + i * stride).  The loads of tile t + NSTAGE - 1 are issued
+// before tile t is computed.  Waits are explicit: `per_tile` is the number of
+// vector-memory instructions this wave issues per load(t, buf) call, and at
+// the end of each step only the tiles after the next one may still be in
+// flight; the barrier then makes every wave's loads visible.
+//   load(t, buf):    issue the loads of tile t into buf
+//   compute(t, buf): use tile t in buf
+template <int NSTAGE, class Load, class Compute>
+__device__ __forceinline__ void run_pipeline(TileWalk walk, int per_tile, char* base, int stride, Load&& load,
+                                             Compute&& compute) {
+  TileWalk ahead = walk;  // walk position of the newest tile issued
+  int issued = 0;         // tiles issued beyond the one being computed
+  if (walk.t >= 0) load(uniform(walk.t), base);
+  for (int st = 1; st < NSTAGE - 1; ++st) {
+    if (ahead.t >= 0) ahead.next();
+    if (ahead.t >= 0) {
+      load(uniform(ahead.t), base + st * stride);
+      ++issued;
+    }
+  }
+  wait_vmem_le(issued * per_tile);
+  __syncthreads();
+  int cur = 0;
+  while (walk.t >= 0) {
+    TileWalk nx = walk;
+    nx.next();
+    if (ahead.t >= 0) ahead.next();
+    if (ahead.t >= 0) {
+      int fill = cur + NSTAGE - 1;
+      load(uniform(ahead.t), base + (fill >= NSTAGE ? fill - NSTAGE : fill) * stride);
+      ++issued;
+    }
+    compute(uniform(walk.t), (const char*)(base + cur * stride));
+    if (nx.t >= 0) --issued;
+    wait_vmem_le(issued * per_tile);
+    __syncthreads();
+    cur = cur + 1 == NSTAGE ? 0 : cur + 1;
+    walk = nx;
+  }
+}
 
 }  // namespace bwattn
