@@ -68,9 +68,12 @@ def cpu_baseline(w, q, k, v, do, seg, pos, budget_s):
         flops = 14.0 * D * float(np.sum(counts[rows]))
         return rows, dt, flops
 
-    rows, dt, flops = run(16)
-    n = int(min(S, max(16, 16 * budget_s / max(dt, 1e-3) * 0.8)))
+    # grow the sample until one run takes about budget_s / 2 .. budget_s
+    n = 16
     rows, dt, flops = run(n)
+    while dt < 0.5 * budget_s and n < S:
+        n = int(min(S, max(2 * n, n * 0.75 * budget_s / max(dt, 1e-3))))
+        rows, dt, flops = run(n)
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
