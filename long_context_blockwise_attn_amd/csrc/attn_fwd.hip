@@ -8,34 +8,40 @@
 // the packing mask (each packed example attends only to itself, 训练方法).
 //
 // Work decomposition: a workgroup of NW waves owns 256 query rows of one
-// (batch, head); each wave owns 32 * QG rows.  Tiles of 64 keys of K and of
-// the transposed V are double-buffered in LDS and filled by direct
-// global-to-LDS loads.  Scores are computed transposed, S^T = K Q^T, so each
-// lane holds one query row: the row max needs one exchange between lanes l
-// and l^32, and the running rescale of O is a per-lane scalar.
-// O^T = V^T P^T takes P^T straight from the score registers; the transposed V
-// copy stores each 16 keys in the order those registers hold them, so both
-// MFMA operands are plain 16-byte LDS reads.
+// (batch, head); each wave owns 32 rows.  Tiles of 64 keys of K and of the
+// transposed V sit in an NSTAGE-deep LDS ring filled by buffer-to-LDS loads.
+// Scores are computed transposed, S^T = K Q^T, so each lane holds one query
+// row: the row max needs one exchange between lanes l and l^32, and the
+// running rescale of O is a per-lane scalar.  O^T = V^T P^T takes P^T straight
+// from the score registers; the transposed V copy stores each 16 keys in the
+// order those registers hold them, so both MFMA operands are plain 16-byte LDS
+// reads.
+//
+// Software pipeline inside each wave, per K/V tile t:
+//   region 1: S^T of tile t+1 (MFMA)  interleaved with  softmax of tile t (VALU)
+//   mask of tile t+1 (only partial tiles)
+//   region 2: O^T += V^T P^T of tile t (MFMA)  interleaved with  row max of t+1
+//   lazy rescale of O for tile t+1 (rare)
+// so the matrix cores and the vector ALUs of a SIMD work at the same time.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "tile.hpp"
 
 namespace bwattn {
 
-template <int D, int NW, int QG, int NSTAGE>
+template <int D, int NW, int NSTAGE>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   constexpr int BQ = kFwdBlockQ, BK = kFwdBlockK;
-  static_assert(BQ == NW * 32 * QG, "query rows per workgroup");
+  static_assert(BQ == NW * 32, "32 query rows per wave");
   static_assert(BK == 64, "two 32-key halves per tile");
-  constexpr int NDC = D / 16;             // 16-wide k steps over D for S^T
-  constexpr int NDG = D / 32;             // 32-row groups of O^T over D
+  static_assert(NSTAGE >= 3, "K of tile t+1 and V of tile t are read in the same step");
+  constexpr int NDC = D / 16;  // 16-wide k steps over D for S^T
+  constexpr int NDG = D / 32;  // 32-row groups of O^T over D
   constexpr float kLazy = 8.f;
-  using KT = PTile<BK, D / 8>;            // K rows
-  using VT = PTile<D, BK / 8>;            // V^T rows (d), 64 keys each
+  using KT = PTile<BK, D / 8>;  // K rows
+  using VT = PTile<D, BK / 8>;  // V^T rows (d), 64 keys each
   constexpr int SEG_OFF = KT::kBytes + VT::kBytes;  // segment ids of the tile's keys
   constexpr int BUF = SEG_OFF + 256;
-  // NSTAGE-deep ring of [K, V^T, seg] tiles: the loads for tile
-  // t + NSTAGE - 1 are in flight while tile t is computed
   __shared__ __attribute__((aligned(16))) char smem[NSTAGE * BUF];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -47,30 +53,26 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   const int S = a.S;
   const int64_t base = (int64_t)bh * S * D;
   const int Q0 = qt * BQ;
-  constexpr int QW = 32 * QG;  // rows per wave
-  const int q0 = Q0 + w * QW;
-  const int qlast = min(S - 1, q0 + QW - 1);
+  const int q0 = Q0 + w * 32;
+  const int row = q0 + l32;  // this lane's query row
   const bool use_seg = a.seg != nullptr;
   const int32_t* segb = use_seg ? a.seg + (int64_t)b * S : nullptr;
   const int2* blkb = use_seg ? a.blk + (int64_t)b * a.nblk : nullptr;
 
-  // Q operand (B of S^T = K Q^T): lane holds row q0 + 32 qg + l32, d = 16 dc + 8 hl + [0,8)
-  bf16x8 qop[QG][NDC];
-  int segq[QG];
-#pragma unroll
-  for (int qg = 0; qg < QG; ++qg) {
-    int row = q0 + 32 * qg + l32;
-    bool ok = row < S;
+  // Q operand (B of S^T = K Q^T): lane holds row `row`, d = 16 dc + 8 hl + [0,8)
+  bf16x8 qop[NDC];
+  {
     const uint16_t* src = a.q + base + (int64_t)min(row, S - 1) * D + 8 * hl;
 #pragma unroll
     for (int dc = 0; dc < NDC; ++dc) {
       bf16x8 v = *(const bf16x8*)(src + 16 * dc);
-      qop[qg][dc] = ok ? v : bf16x8{};
+      qop[dc] = row < S ? v : bf16x8{};
     }
-    segq[qg] = (use_seg && ok) ? segb[row] : 0;
   }
+  const int segq = (use_seg && row < S) ? segb[row] : 0;
+  const int segsel = use_seg ? -1 : 0;  // the LDS segment ids are ignored without packing
   int2 wrange = make_int2(0, 0);
-  if (use_seg && q0 < S) wrange = seg_range(blkb, a.nblk, q0, min(QW, S - q0));
+  if (use_seg && q0 < S) wrange = seg_range(blkb, a.nblk, q0, min(32, S - q0));
 
   // K/V tile range and walk
   TileWalk walk;
@@ -93,16 +95,12 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   walk.own = use_seg ? seg_range(blkb, a.nblk, Q0, min(BQ, S - Q0)) : make_int2(0, 0);
   walk.start();
 
-  float m[QG], lsum[QG];
-  f32x16 o[QG][NDG];
+  float m = kNegInf, lsum = 0.f;
+  f32x16 o[NDG];
 #pragma unroll
-  for (int qg = 0; qg < QG; ++qg) {
-    m[qg] = kNegInf;
-    lsum[qg] = 0.f;
-#pragma unroll
-    for (int dg = 0; dg < NDG; ++dg) o[qg][dg] = f32x16{};
-  }
+  for (int dg = 0; dg < NDG; ++dg) o[dg] = f32x16{};
   const float sl2 = a.scale_log2;
+
   const uint16_t* kh = a.k + base;
   const uint16_t* vth = a.vt + (int64_t)bh * D * a.sp;
   TileFill<BK, D / 8, NW> kfill;  // K rows
@@ -116,139 +114,203 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   };
   // vector-memory instructions this wave issues per tile
   const int per_tile = kfill.count() + vfill.count() + (use_seg && w == 0 ? 1 : 0);
-  auto compute = [&](int t, const char* buf) {
-    const int k0 = t * BK;
-    bool skip = q0 >= S || (a.causal && k0 > qlast);
-    bool seg_mask = false;
-    if (use_seg && !skip) {
-      int2 kr = seg_range(blkb, a.nblk, k0, BK);
-      if (!ranges_meet(kr, wrange))
-        skip = true;
-      else
-        seg_mask = !(kr.x == kr.y && wrange.x == wrange.y && kr.x == wrange.x);
-    }
-    if (!skip) {
-      const char* kt = buf;
-      const char* vt = buf + KT::kBytes;
-      const int* segk_lds = (const int*)(buf + SEG_OFF);
-      // S^T = K Q^T for both 32-key halves (independent accumulator chains):
-      // s[qg][kg] holds keys k0 + 32 kg + 8 (r/4) + 4 hl + r%4 of row l32
-      f32x16 s[QG][2];
-#pragma unroll
-      for (int qg = 0; qg < QG; ++qg) s[qg][0] = s[qg][1] = f32x16{};
-#pragma unroll
-      for (int dc = 0; dc < NDC; ++dc) {
-#pragma unroll
-        for (int kg = 0; kg < 2; ++kg) {
-          bf16x8 ka = KT::read(kt, 32 * kg, dc, lane);
-#pragma unroll
-          for (int qg = 0; qg < QG; ++qg) s[qg][kg] = mfma32(ka, qop[qg][dc], s[qg][kg]);
-        }
-      }
-      if (seg_mask || (k0 + BK > S) || (a.causal && k0 + BK - 1 > q0)) {
-        // partial tile: causal, segment and sequence-end masks
-        int jb = k0 + 4 * hl;
-#pragma unroll
-        for (int kg = 0; kg < 2; ++kg)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            int j = jb + 32 * kg + 8 * (r >> 2) + (r & 3);
-            int sk = 0;
-            if (use_seg) sk = segk_lds[j - k0];
-#pragma unroll
-            for (int qg = 0; qg < QG; ++qg) {
-              int i = q0 + 32 * qg + l32;
-              bool vis = j < S && (!a.causal || j <= i) && (!use_seg || sk == segq[qg]);
-              s[qg][kg][r] = vis ? s[qg][kg][r] : kNegInf;
-            }
-          }
-      }
-#pragma unroll
-      for (int kg = 0; kg < 2; ++kg) {
-        // Online softmax merge.  A row's running max m is raised only when
-        // its new max exceeds it by more than kLazy (log2 units); otherwise
-        // the stale m stays, p <= 2^kLazy, and O is not touched.  l and O
-        // share m, so the normalised result is unchanged.  The decision is
-        // per row (the wave only branches when some row needs it), so a
-        // row's result depends on its own visible keys alone.
-        bf16x8 pk[QG][2];
-#pragma unroll
-        for (int qg = 0; qg < QG; ++qg) {
-          f32x16& sv = s[qg][kg];
-          float mx = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
-#pragma unroll
-          for (int r = 3; r < 15; r += 2) mx = fmaxf(fmaxf(mx, sv[r]), sv[r + 1]);
-          mx = fmaxf(mx, sv[15]);
-          mx = pair_max(mx) * sl2;
-          const bool grow = mx > m[qg] + kLazy;
-          if (__ballot(grow)) {
-            float mnew = grow ? fmaxf(m[qg], mx) : m[qg];
-            float alpha = fast_exp2(m[qg] - (mnew == kNegInf ? 0.f : mnew));  // 1 when m stays
-            lsum[qg] *= alpha;
-#pragma unroll
-            for (int dg = 0; dg < NDG; ++dg) o[qg][dg] *= alpha;
-            m[qg] = mnew;
-          }
-          const float muse = (m[qg] == kNegInf) ? 0.f : m[qg];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sv[r] = fast_exp2(__builtin_fmaf(sv[r], sl2, -muse));
-          // P in bf16 feeds the MFMA; the row sum adds the same bf16 values
-          float rs = lsum[qg];
-#pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            int r0 = 8 * c;
-            u32x4 pw = {pack_bf16x2(sv[r0], sv[r0 + 1]), pack_bf16x2(sv[r0 + 2], sv[r0 + 3]),
-                        pack_bf16x2(sv[r0 + 4], sv[r0 + 5]), pack_bf16x2(sv[r0 + 6], sv[r0 + 7])};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) rs = dot2_bf16(pw[e], kBf16OnePair, rs);
-            pk[qg][c] = __builtin_bit_cast(bf16x8, pw);
-          }
-          lsum[qg] = rs;
-        }
-        // O^T += V^T P^T over the 32 keys of this half
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-#pragma unroll
-          for (int dg = 0; dg < NDG; ++dg) {
-            bf16x8 va = VT::read(vt, 32 * dg, 2 * kg + c, lane);
-#pragma unroll
-            for (int qg = 0; qg < QG; ++qg) o[qg][dg] = mfma32(va, pk[qg][c], o[qg][dg]);
-          }
-        }
-      }
-    }
-  };
-  run_pipeline<NSTAGE>(walk, per_tile, smem, BUF, load, compute);
 
-  // epilogue: O = O^T / l, LSE = ln2 (m + log2 l)
+  // --- per-tile pieces -----------------------------------------------------
+  // S^T of the tile in `buf`: s[kg] holds keys k0 + 32 kg + 8 (r/4) + 4 hl + r%4
+  auto scores = [&](const char* buf, f32x16 (&s)[2]) {
+    s[0] = s[1] = f32x16{};
 #pragma unroll
-  for (int qg = 0; qg < QG; ++qg) {
-    int row = q0 + 32 * qg + l32;
-    float lt = pair_sum(lsum[qg]);
-    float inv = 1.f / lt;
-    if (row < S) {
-      uint16_t* dst = a.o + base + (int64_t)row * D + 4 * hl;
+    for (int dc = 0; dc < NDC; ++dc)
 #pragma unroll
-      for (int dg = 0; dg < NDG; ++dg)
+      for (int kg = 0; kg < 2; ++kg) s[kg] = mfma32(KT::read(buf, 32 * kg, dc, lane), qop[dc], s[kg]);
+  };
+  // causal / segment / sequence-end mask of tile t (wave-uniform decision)
+  auto mask = [&](int t, const char* buf, f32x16 (&s)[2]) {
+    const int k0 = t * BK;
+    bool seg_mask = false;
+    if (use_seg) {
+      int2 kr = seg_range(blkb, a.nblk, k0, BK);
+      seg_mask = !(kr.x == kr.y && wrange.x == wrange.y && kr.x == wrange.x);
+    }
+    if (seg_mask || (k0 + BK > S) || (a.causal && k0 + BK - 1 > q0)) {
+      const int* segk = (const int*)(buf + SEG_OFF);
+      const int lim = a.causal ? min(S - 1, row) : S - 1;  // last visible key of this row
+#pragma unroll
+      for (int kg = 0; kg < 2; ++kg)
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
-          const f32x16& ov = o[qg][dg];
-          uint32_t w0 = pack_bf16x2(ov[4 * rq] * inv, ov[4 * rq + 1] * inv);
-          uint32_t w1 = pack_bf16x2(ov[4 * rq + 2] * inv, ov[4 * rq + 3] * inv);
-          *(u32x2*)(dst + 32 * dg + 8 * rq) = u32x2{w0, w1};
+          const int jj = 32 * kg + 8 * rq + 4 * hl;  // keys jj .. jj+3 in registers 4 rq ..
+          const int4 sk = *(const int4*)(segk + jj);
+          const int sk_[4] = {sk.x, sk.y, sk.z, sk.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool vis = (k0 + jj + e <= lim) & (((sk_[e] ^ segq) & segsel) == 0);
+            s[kg][4 * rq + e] = vis ? s[kg][4 * rq + e] : kNegInf;
+          }
         }
-      if (hl == 0) a.lse[(int64_t)bh * S + row] = (m[qg] + __log2f(lt)) * kLn2;
     }
+  };
+  // Row max of a tile's raw scores, in log2 units of the scaled scores.
+  auto tile_max = [&](const f32x16 (&s)[2]) {
+    float mx = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(fmaxf(mx, s[0][r]), s[1][r]);
+    return pair_max(mx) * sl2;
+  };
+  // Lazy online-softmax max update.  A row's running max m is raised only
+  // when its new max exceeds it by more than kLazy (log2 units); otherwise
+  // the stale m stays, p <= 2^kLazy, and O is not touched.  l and O share m,
+  // so the normalised result is unchanged.  The decision is per row (the
+  // wave only branches when some row needs it), so a row's result depends on
+  // its own visible keys alone.
+  auto rescale = [&](float mx) {
+    const bool grow = mx > m + kLazy;
+    if (__ballot(grow)) {
+      float mnew = grow ? fmaxf(m, mx) : m;
+      float alpha = fast_exp2(m - (mnew == kNegInf ? 0.f : mnew));  // 1 when m stays
+      lsum *= alpha;
+#pragma unroll
+      for (int dg = 0; dg < NDG; ++dg) o[dg] *= alpha;
+      m = mnew;
+    }
+  };
+  // P = 2^(S*scale*log2e - m) as bf16 MFMA operands pk[kc] (keys 16 kc ..),
+  // and the row sum over the same bf16 values
+  auto softmax = [&](const f32x16 (&s)[2], bf16x8 (&pk)[4]) {
+    const float muse = (m == kNegInf) ? 0.f : m;
+    float rs = lsum;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const int r0 = 8 * (kc & 1);
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p[e] = fast_exp2(__builtin_fmaf(s[kc >> 1][r0 + e], sl2, -muse));
+      u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                  pack_bf16x2(p[6], p[7])};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rs = dot2_bf16(pw[e], kBf16OnePair, rs);
+      pk[kc] = __builtin_bit_cast(bf16x8, pw);
+    }
+    lsum = rs;
+  };
+  auto pv = [&](const char* buf, const bf16x8 (&pk)[4]) {
+    const char* vt = buf + KT::kBytes;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+      for (int dg = 0; dg < NDG; ++dg) o[dg] = mfma32(VT::read(vt, 32 * dg, kc, lane), pk[kc], o[dg]);
+  };
+
+  // --- ping-pong pipeline -------------------------------------------------
+  // Waves 0-3 and 4-7 form two groups with one wave of each on every SIMD.
+  // Each step has a matrix phase (S^T of tile k+1, O^T += V^T P^T of tile k)
+  // and a vector phase (mask, max, rescale and softmax of tile k+1).  Group 1
+  // runs one barrier behind group 0, so on every SIMD one wave issues MFMAs
+  // while the other runs the softmax, and they swap at each barrier.
+  // Barrier G_j: group 0 runs the matrix phase of step k between G_2k and
+  // G_2k+1, group 1 between G_2k+1 and G_2k+2.  Tile position p lives in ring
+  // slot p % 4; it is read from G_2p-2 (K of p in the matrix phase of step
+  // p-1) until G_2p+2 (V of p in group 1's matrix phase of step p).  So each
+  // wave issues position k+4 right after G_2k+2 and, before G_2k+2, waits for
+  // its loads of position k+2 (only k+3 may still be in flight).
+  static_assert(NW == 8 && NSTAGE == 4, "two groups of four waves, four-slot ring");
+  const int grp = uniform(w >> 2);
+  auto slot = [&](int p) { return smem + (p & (NSTAGE - 1)) * BUF; };
+  if (walk.t >= 0) {
+    TileWalk w1 = walk;  // position k + 1
+    w1.next();
+    TileWalk ahead = w1;  // newest position issued
+    load(uniform(walk.t), slot(0));
+    int pend = 0;
+    if (w1.t >= 0) {
+      load(uniform(w1.t), slot(1));
+#pragma unroll
+      for (int p = 2; p < NSTAGE; ++p) {
+        if (ahead.t >= 0) ahead.next();
+        if (ahead.t >= 0) {
+          load(uniform(ahead.t), slot(p));
+          ++pend;
+        }
+      }
+    }
+    int ahead_pos = 1 + pend;  // position of `ahead` when it is valid
+    wait_vmem_le(pend * per_tile);
+    __syncthreads();  // G_0
+
+    bf16x8 pk[4];
+    {
+      f32x16 s0[2];
+      scores(slot(0), s0);
+      mask(uniform(walk.t), slot(0), s0);
+      rescale(tile_max(s0));
+      softmax(s0, pk);
+    }
+    if (grp == 1) __syncthreads();  // G_1: group 1 starts one phase later
+
+    // wait for position k+2 (k+3 may be in flight), barrier, issue k+4
+    auto refill = [&](int k) {
+      wait_vmem_le((ahead.t >= 0 && ahead_pos >= k + 3) ? per_tile : 0);
+      __syncthreads();
+      if (ahead.t >= 0) ahead.next();
+      if (ahead.t >= 0) {
+        ++ahead_pos;
+        load(uniform(ahead.t), slot(ahead_pos));
+      }
+    };
+
+    int k = 0;
+    while (walk.t >= 0) {
+      const bool more = w1.t >= 0;
+      f32x16 s_next[2];
+      __builtin_amdgcn_s_setprio(1);
+      if (more) scores(slot(k + 1), s_next);
+      pv(slot(k), pk);
+      __builtin_amdgcn_s_setprio(0);
+      if (grp == 0)
+        __syncthreads();
+      else
+        refill(k);
+      if (more) {
+        mask(uniform(w1.t), slot(k + 1), s_next);
+        rescale(tile_max(s_next));
+        softmax(s_next, pk);
+      }
+      if (grp == 0)
+        refill(k);
+      else
+        __syncthreads();
+      walk = w1;
+      if (w1.t >= 0) w1.next();
+      ++k;
+    }
+    if (grp == 0) __syncthreads();  // matches group 1's extra barrier
+  }
+
+  // epilogue: O = O^T / l, LSE = ln2 (m + log2 l)
+  const float lt = pair_sum(lsum);
+  const float inv = 1.f / lt;
+  if (row < S) {
+    uint16_t* dst = a.o + base + (int64_t)row * D + 4 * hl;
+#pragma unroll
+    for (int dg = 0; dg < NDG; ++dg)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const f32x16& ov = o[dg];
+        uint32_t w0 = pack_bf16x2(ov[4 * rq] * inv, ov[4 * rq + 1] * inv);
+        uint32_t w1 = pack_bf16x2(ov[4 * rq + 2] * inv, ov[4 * rq + 3] * inv);
+        *(u32x2*)(dst + 32 * dg + 8 * rq) = u32x2{w0, w1};
+      }
+    if (hl == 0) a.lse[(int64_t)bh * S + row] = (m + __log2f(lt)) * kLn2;
   }
 }
 
 hipError_t launch_attn_fwd(const FwdArgs& a, int D, hipStream_t st) {
-  constexpr int NW = 8, QG = 1, NSTAGE = 3;
+  constexpr int NW = 8, NSTAGE = 4;
   dim3 grid((unsigned)((int64_t)a.B * a.H * a.n_qtiles)), block(NW * 64);
   if (D == 128)
-    hipLaunchKernelGGL((attn_fwd_kernel<128, NW, QG, NSTAGE>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<128, NW, NSTAGE>), grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<64, NW, QG, NSTAGE>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<64, NW, NSTAGE>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 

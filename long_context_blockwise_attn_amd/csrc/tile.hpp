@@ -26,6 +26,10 @@ struct PTile {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
+// A value the caller knows to be the same in every lane, held in a scalar
+// register so that branches on it are wave-level jumps.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 // Raw buffer resource over `bytes` bytes from `base` (stride 0): loads at
 // offsets past the end return zero.  Word 3 is the raw-buffer format word of
 // gfx9.  The value is uniform across the wave.
@@ -69,7 +73,7 @@ struct TileFill {
   uint32_t voff[kPer];
   int w;
   __device__ void init(uint32_t row_bytes, int tid) {
-    w = tid >> 6;
+    w = uniform(tid >> 6);
     const int lane = tid & 63;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
@@ -98,6 +102,9 @@ __device__ __forceinline__ void row64_to_lds(const void* src, int i0, int n, cha
   dma_b32(rs, dst, lane * 4);
 }
 
+// scheduling-group masks of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedVALU = 0x002, kSchedMFMA = 0x008, kSchedDSRead = 0x100;
+
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0); }
 
 // Wait until at most n vector-memory operations of this wave are in flight
@@ -106,7 +113,7 @@ __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0); }
 __device__ __forceinline__ void wait_vmem_le(int n) {
 #define BWATTN_VMCNT(k) \
   case k: __builtin_amdgcn_s_waitcnt(((k) & 15) | (((k) >> 4) << 14) | 0x0F70); break;
-  switch (n) {
+  switch (uniform(n)) {
     BWATTN_VMCNT(0) BWATTN_VMCNT(1) BWATTN_VMCNT(2) BWATTN_VMCNT(3) BWATTN_VMCNT(4) BWATTN_VMCNT(5)
     BWATTN_VMCNT(6) BWATTN_VMCNT(7) BWATTN_VMCNT(8) BWATTN_VMCNT(9) BWATTN_VMCNT(10) BWATTN_VMCNT(11)
     BWATTN_VMCNT(12) BWATTN_VMCNT(13) BWATTN_VMCNT(14) BWATTN_VMCNT(15) BWATTN_VMCNT(16) BWATTN_VMCNT(17)
@@ -137,7 +144,6 @@ __device__ __forceinline__ int2 range_union(int2 a, int2 b) { return make_int2(m
 __device__ __forceinline__ bool ranges_meet(int2 a, int2 b) { return !(a.y < b.x || a.x > b.y); }
 
 // Segment-id range of rows [r0, r0 + rows) from the 32-row block ranges.
-__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // (r0 and rows are uniform across the wave; the loads are scalar.)
 __device__ __forceinline__ int2 seg_range(const int2* blk, int nblk, int r0, int rows) {
@@ -159,7 +165,7 @@ __device__ __forceinline__ int2 seg_range(const int2* blk, int nblk, int r0, int
 // uniform across the workgroup.
 struct TileWalk {
   int lo, hi, ct, nc, r, dir;
-  bool desc;  // natural order (ct == 0) only: visit hi-1 down to lo
+  int desc;  // natural order (ct == 0) only, nonzero: visit hi-1 down to lo
   int step, t;
   const int2* blk;
   int nblk, rows;
