@@ -175,13 +175,14 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int kg = 0; kg < 2; ++kg) {
         f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-        for (int dc = 0; dc < NDC; ++dc) {
-          bf16x8 ka = KT::read(ktl, 32 * kg, dc, lane);
-          bf16x8 va = KT::read(vtl, 32 * kg, dc, lane);
-          s = mfma32(ka, qop[dc], s);
-          dp = mfma32(va, dop[dc], dp);
-        }
+        lds_mfma_pipe<2 * NDC, 6>(
+            [&](int i) { return KT::read((i & 1) ? vtl : ktl, 32 * kg, i >> 1, lane); },
+            [&](int i, bf16x8 x) {
+              if (i & 1)
+                dp = mfma32(x, dop[i >> 1], dp);
+              else
+                s = mfma32(x, qop[i >> 1], s);
+            });
         if (need_mask) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
@@ -205,14 +206,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
                                                     pack_bf16x2(s[r0 + 4], s[r0 + 5]), pack_bf16x2(s[r0 + 6], s[r0 + 7])});
         }
         // dQ^T += K^T dS^T over the 32 keys of this half
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-#pragma unroll
-          for (int dg = 0; dg < NDG; ++dg) {
-            bf16x8 kta = KTT::read(kttl, 32 * dg, 2 * kg + c, lane);
-            dq[dg] = mfma32(kta, dsk[c], dq[dg]);
-          }
-        }
+        lds_mfma_pipe<2 * NDG, 6>([&](int i) { return KTT::read(kttl, 32 * (i % NDG), 2 * kg + i / NDG, lane); },
+                                  [&](int i, bf16x8 x) { dq[i % NDG] = mfma32(x, dsk[i / NDG], dq[i % NDG]); });
       }
     }
   };

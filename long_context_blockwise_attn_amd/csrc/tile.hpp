@@ -130,6 +130,25 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// N (LDS read, MFMA) pairs with the read of pair i issued LA pairs ahead of
+// the MFMA that consumes it: rd(i) returns operand i, mm(i, x) issues MFMA i.
+// Scheduling fences hold that order; left alone, the compiler tends to reuse
+// one register and wait on every read, which leaves the matrix core waiting
+// on LDS latency.
+template <int N, int LA, class Rd, class Mm>
+__device__ __forceinline__ void lds_mfma_pipe(Rd&& rd, Mm&& mm) {
+  bf16x8 r[N];
+#pragma unroll
+  for (int i = 0; i < LA && i < N; ++i) r[i] = rd(i);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (i + LA < N) r[i + LA] = rd(i + LA);
+    mm(i, r[i]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Max and sum over the two lanes l and l ^ 32 (v_permlane32_swap).
 __device__ __forceinline__ float pair_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
