@@ -108,9 +108,12 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
     }
     dsum = pair_sum(dsum);
     delta = ok ? dsum : 0.f;
-    if (ok && hl == 0) a.delta[(int64_t)bh * S + row] = dsum;
   }
   const float nlse2 = ok ? -a.lse[(int64_t)bh * S + row] * kLog2e : 0.f;
+  if (ok && hl == 0) {  // row statistics for the dK/dV kernel
+    a.ndelta[(int64_t)bh * S + row] = -delta;
+    a.nlse2[(int64_t)bh * S + row] = nlse2;
+  }
   const int segq = (use_seg && ok) ? segb[row] : 0;
   const int qlast = min(S - 1, q0 + 31);
   int2 wrange = make_int2(0, 0);
@@ -174,7 +177,10 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
       const bool need_mask = seg_mask || (k0 + BK > S) || (a.causal && k0 + BK - 1 > q0);
 #pragma unroll
       for (int kg = 0; kg < 2; ++kg) {
-        f32x16 s = f32x16{}, dp = f32x16{};
+        // dP^T starts from -Delta, so the MFMAs leave dP^T - Delta
+        f32x16 s = f32x16{}, dp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[r] = -delta;
         lds_mfma_pipe<2 * NDC, 6>(
             [&](int i) { return KT::read((i & 1) ? vtl : ktl, 32 * kg, i >> 1, lane); },
             [&](int i, bf16x8 x) {
@@ -195,10 +201,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
         }
         bf16x8 dsk[2];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(__builtin_fmaf(s[r], sl2, nlse2));
-          s[r] = p * (dp[r] - delta);
-        }
+        for (int r = 0; r < 16; ++r) s[r] = fast_exp2(__builtin_fmaf(s[r], sl2, nlse2)) * dp[r];
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           int r0 = 8 * c;
@@ -235,7 +238,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NDC = D / 16, NDG = D / 32;
   using QT = PTile<BQT, D / 8>;   // Q and dO rows
   using QTT = PTile<D, BQT / 8>;  // Q^T and dO^T rows (d), 64 query rows each
-  constexpr int SB = 2 * QT::kBytes + 2 * QTT::kBytes;  // row statistics: LSE[64], Delta[64], seg[64]
+  constexpr int SB = 2 * QT::kBytes + 2 * QTT::kBytes;  // row statistics: -LSE log2e [64], -Delta [64], seg [64]
   constexpr int BUF = SB + 3 * 256;
   // ring of [Q, dO, Q^T, dO^T, statistics] stages (see run_pipeline)
   __shared__ __attribute__((aligned(16))) char smem[NSTAGE * BUF];
@@ -301,11 +304,11 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
   const uint16_t* dh = a.dout + base;
   const uint16_t* qth = a.qt + (int64_t)bh * D * a.sp;
   const uint16_t* dth = a.dot + (int64_t)bh * D * a.sp;
-  const float* lse_h = a.lse + (int64_t)bh * S;
-  const float* del_h = a.delta + (int64_t)bh * S;
+  const float* nlse_h = a.nlse2 + (int64_t)bh * S;
+  const float* ndel_h = a.ndelta + (int64_t)bh * S;
 
-  // tiles of a Q block and its row statistics (LSE, Delta, segment id),
-  // the statistics fetched by wave 0
+  // tiles of a Q block and its row statistics (-LSE log2(e), -Delta,
+  // segment id), the statistics fetched by wave 0
   TileFill<BQT, D / 8, NW> rfill;  // Q and dO rows
   TileFill<D, BQT / 8, NW> tfill;  // Q^T and dO^T rows
   rfill.init(D * 2, tid);
@@ -318,8 +321,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
     tfill.fill(qth + t * BQT, tbytes, buf + 2 * QT::kBytes);
     tfill.fill(dth + t * BQT, tbytes, buf + 2 * QT::kBytes + QTT::kBytes);
     if (w == 0) {
-      row64_to_lds(lse_h, t * BQT, S, buf + SB, lane);
-      row64_to_lds(del_h, t * BQT, S, buf + SB + 256, lane);
+      row64_to_lds(nlse_h, t * BQT, S, buf + SB, lane);
+      row64_to_lds(ndel_h, t * BQT, S, buf + SB + 256, lane);
       if (use_seg) row64_to_lds(segb, t * BQT, S, buf + SB + 512, lane);
     }
   };
@@ -374,13 +377,13 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
           for (int hq = 0; hq < 2; ++hq) {
             const int rq = 2 * c + hq;
             const int ri = 32 * qg + 8 * rq + 4 * hl;
-            const f32x4 nl = *(const f32x4*)(st + ri) * -kLog2e;
-            const f32x4 de = *(const f32x4*)(st + 64 + ri);
+            const f32x4 nl = *(const f32x4*)(st + ri);
+            const f32x4 nd = *(const f32x4*)(st + 64 + ri);
             float pv[4], dsv[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               pv[e] = fast_exp2(__builtin_fmaf(s[4 * rq + e], sl2, nl[e]));
-              dsv[e] = pv[e] * (dp[4 * rq + e] - de[e]);
+              dsv[e] = pv[e] * (dp[4 * rq + e] + nd[e]);
             }
             pw[2 * hq] = pack_bf16x2(pv[0], pv[1]);
             pw[2 * hq + 1] = pack_bf16x2(pv[2], pv[3]);

@@ -127,8 +127,8 @@ Plan make_plan(const attn_params* p, int which) {
     off += align256(nt * 2);
     pl.off_dot = off;
     off += align256(nt * 2);
-    pl.off_delta = off;
-    off += align256((size_t)pl.B * pl.H * pl.S * 4);
+    pl.off_delta = off;  // -Delta, then -LSE log2(e)
+    off += 2 * align256((size_t)pl.B * pl.H * pl.S * 4);
   }
   pl.off_blk = off;
   off += align256((size_t)pl.B * pl.nblk * sizeof(int2));
@@ -384,7 +384,8 @@ int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v, 
   a.o = (const uint16_t*)o;
   a.dout = (const uint16_t*)d_o;
   a.lse = lse;
-  a.delta = (float*)(ws + pl.off_delta);
+  a.ndelta = (float*)(ws + pl.off_delta);
+  a.nlse2 = (float*)(ws + pl.off_delta + align256((size_t)pl.B * pl.H * pl.S * 4));
   a.dq = (uint16_t*)dq;
   a.dk = (uint16_t*)dk;
   a.dv = (uint16_t*)dv;

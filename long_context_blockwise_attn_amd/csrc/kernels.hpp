@@ -71,7 +71,8 @@ struct BwdArgs {
   const uint16_t* o;
   const uint16_t* dout;
   const float* lse;    // natural log
-  float* delta;        // [B,H,S] workspace: <dO_i, O_i>
+  float* ndelta;       // [B,H,S] workspace written by the dQ kernel: -<dO_i, O_i>
+  float* nlse2;        // [B,H,S] workspace written by the dQ kernel: -LSE_i log2(e)
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
