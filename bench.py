@@ -85,6 +85,86 @@ def cpu_baseline(w, q, k, v, do, seg, pos, budget_s):
     }
 
 
+# rocprofv3 kernel-name fragments of the timed kernels
+KERNEL_SYMBOLS = {"fwd": "attn_fwd_kernel", "bwd_dq": "attn_bwd_dq_kernel", "bwd_dkdv": "attn_bwd_dkdv_kernel"}
+
+
+def kernel_source_hash():
+    """sha256 over the HIP/C++ sources of the library: a traffic record is
+    only used while the kernels are the ones it was measured on."""
+    import hashlib
+
+    d = os.path.join(ROOT, "long_context_blockwise_attn_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".hpp", ".cpp", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_path(workload):
+    return os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+
+
+def counter_rows(path, counter):
+    """(kernel name, dispatch id, value) of one counter from a rocprofv3
+    counter_collection CSV, in dispatch order."""
+    import csv
+
+    out = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                out.append((r["Kernel_Name"], int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+    out.sort(key=lambda x: x[1])
+    return out
+
+
+def write_traffic_record(workload, fetch_csv, write_csv, copy_mib, command):
+    """HBM bytes per launch of each timed kernel from two rocprofv3 --pmc
+    runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by the
+    factor that makes the last plain copy of the run (copy_mib MiB read and
+    written) read exactly its size."""
+    rec = {"workload": workload, "source_sha256": kernel_source_hash(), "command": command, "kernels": {}}
+    copy_bytes = float(copy_mib) * (1 << 20)
+    for counter, path, key in (("FETCH_SIZE", fetch_csv, "read"), ("WRITE_SIZE", write_csv, "write")):
+        rows = counter_rows(path, counter)
+        copies = [r for r in rows if "copy" in r[0].lower()]
+        if not copies:
+            raise SystemExit("no copy kernel in %s" % path)
+        cal_kib = copies[-1][2]
+        factor = copy_bytes / (cal_kib * 1024.0)
+        rec["%s_calibration" % key] = {"copy_bytes": copy_bytes, "counter_kib": cal_kib, "factor": factor}
+        for name, sym in KERNEL_SYMBOLS.items():
+            vals = [r[2] for r in rows if sym in r[0]]
+            if vals:
+                k = rec["kernels"].setdefault(name, {})
+                k["%s_counter_kib" % key] = float(np.mean(vals))
+                k["%s_bytes" % key] = float(np.mean(vals)) * 1024.0 * factor
+                k["dispatches"] = len(vals)
+    for k in rec["kernels"].values():
+        k["traffic_bytes"] = k.get("read_bytes", 0.0) + k.get("write_bytes", 0.0)
+    with open(traffic_path(workload), "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
+def load_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the stored record, or None when
+    there is none or the kernels changed since it was measured."""
+    try:
+        with open(traffic_path(workload)) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("traffic_bytes")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -93,10 +173,19 @@ def main():
     ap.add_argument("--workload", default="llama7b_32k",
                     help="llama7b_32k (default), packing_128k, video_text_256k, full_1m, tiny")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=24.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (HBM counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the HBM traffic record of --workload from two rocprofv3 --pmc counter CSVs "
+                         "(FETCH_SIZE, WRITE_SIZE) of runs made with --copy-calibration-mib, then exit")
+    ap.add_argument("--traffic-command", default="", help="command line recorded with --traffic-from")
     args = ap.parse_args()
+
+    if args.traffic_from:
+        write_traffic_record(args.workload, args.traffic_from[0], args.traffic_from[1],
+                             args.copy_calibration_mib or 1024, args.traffic_command)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path (asked for %d GPUs)" % args.gpus,
@@ -195,8 +284,8 @@ def main():
     dom_flops = contractions[dom] * 2.0 * D * H * pairs
     dom_tflops = dom_flops / (kernel_ms[dom]["avg_ms"] * 1e-3) / 1e12
     roofline = {"kernel": dom, "bound": "mfma", "achieved": dom_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": dom_tflops / BF16_PEAK_TFLOPS, "traffic": None,
-                "flops_per_launch": dom_flops}
+                "frac": dom_tflops / BF16_PEAK_TFLOPS, "traffic": load_traffic(w.name, dom),
+                "traffic_unit": "HBM bytes per launch", "flops_per_launch": dom_flops}
 
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20

@@ -6,7 +6,7 @@
 namespace bwattn {
 
 // Tile sizes shared by the host schedule and the kernels.
-constexpr int kFwdBlockQ = 256;   // query rows per forward / dQ workgroup (4 waves x 64 rows)
+constexpr int kFwdBlockQ = 256;   // query rows per forward / dQ workgroup (8 waves x 32 rows)
 constexpr int kFwdBlockK = 64;    // keys per K/V tile streamed by the forward / dQ kernels
 constexpr int kBwdBlockK = 256;   // keys per dK/dV workgroup (8 waves x 32 keys)
 constexpr int kBwdBlockQ = 64;    // query rows per Q/dO tile streamed by the dK/dV kernel
