@@ -118,6 +118,34 @@ int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v, 
              const float* lse, const void* d_o, const int32_t* segment_ids, const int32_t* positions,
              void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Decode attention against a long key/value cache: the n_q new query rows
+ * of each (b, h) against the p->seqlen = S cached keys, as in 1M-token
+ * inference with the same exact blockwise attention (zhao9797 page "LWM
+ * (Large World Model)", 模型架构).  The keys are split into chunks (split-K);
+ * each chunk keeps the online-softmax state (running max, running sum,
+ * unnormalised output) of every row, and the chunks are merged with the same
+ * rule.
+ *   - q: bf16 [B,H,n_q,D], un-rotated.  Query row r is the token at sequence
+ *     index S - n_q + r: the cache already holds its key and value.  With
+ *     p->causal = 1 it sees keys j <= S - n_q + r, otherwise all S keys.
+ *   - k_cache: bf16 [B,H,S,D] keys already rotated (rope_apply at their
+ *     positions, done once when a key enters the cache); un-rotated when
+ *     rope_theta <= 0.  v_cache: bf16 [B,H,S,D].
+ *   - q_positions: int32 [B,n_q] RoPE positions of the query rows; NULL means
+ *     S - n_q + r.
+ *   - o: bf16 [B,H,n_q,D]; lse: fp32 [B,H,n_q] (natural log).
+ *   - 1 <= n_q <= 32; segment masks are not taken (one document per row);
+ *     p->kv_chunk and p->deterministic are ignored.  The result does not
+ *     depend on the split.
+ * workspace: attn_decode_workspace_bytes(p, n_q) bytes of device memory. */
+int attn_decode(const attn_params* p, int32_t n_q, const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* q_positions, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                void* stream);
+
+/* Bytes of device workspace attn_decode needs for these parameters and n_q;
+ * 0 if they are invalid. */
+size_t attn_decode_workspace_bytes(const attn_params* p, int32_t n_q);
+
 /* ------------------------------------------------------------------------ */
 /* Measurement hook (for benchmarks and profilers; not needed to compute).    */
 /* ------------------------------------------------------------------------ */
@@ -126,7 +154,9 @@ typedef enum {
   ATTN_KERNEL_FWD = 1,       /* forward main kernel                                   */
   ATTN_KERNEL_BWD_DQ = 2,    /* backward: dQ and Delta                                */
   ATTN_KERNEL_BWD_DKDV = 3,  /* backward: dK and dV                                   */
-  ATTN_KERNEL_COUNT = 4
+  ATTN_KERNEL_DECODE = 4,    /* decode: per-chunk partial states (split-K)            */
+  ATTN_KERNEL_DECODE_MERGE = 5, /* decode: merge of the chunk states                  */
+  ATTN_KERNEL_COUNT = 6
 } attn_kernel_id;
 
 /* Ask the library to bracket the next n launches of kernel `kernel` made by

@@ -11,7 +11,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["attn_fwd", "attn_bwd", "rope_apply", "workspace_bytes", "AttnError", "library_path", "Params"]
+__all__ = ["attn_fwd", "attn_bwd", "attn_decode", "rope_apply", "workspace_bytes", "decode_workspace_bytes", "AttnError",
+           "library_path", "Params"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libbwattn.so")
@@ -64,6 +65,10 @@ def load():
         lib.attn_fwd.argtypes = [P, V, V, V, V, V, V, V, V, ctypes.c_size_t, V]
         lib.attn_bwd.restype = ctypes.c_int
         lib.attn_bwd.argtypes = [P, V, V, V, V, V, V, V, V, V, V, V, V, ctypes.c_size_t, V]
+        lib.attn_decode.restype = ctypes.c_int
+        lib.attn_decode.argtypes = [P, ctypes.c_int32, V, V, V, V, V, V, V, ctypes.c_size_t, V]
+        lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
+        lib.attn_decode_workspace_bytes.argtypes = [P, ctypes.c_int32]
         lib.attn_profile_events.restype = ctypes.c_int
         lib.attn_profile_events.argtypes = [ctypes.c_int32, V, V, ctypes.c_int32]
         lib.attn_profile_count.restype = ctypes.c_int32
@@ -186,3 +191,40 @@ def attn_bwd(q, k, v, o, lse, dout, segment_ids=None, positions=None, theta=0.0,
                            _ptr(segment_ids), _ptr(positions), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), nbytes,
                            _stream()))
     return dq, dk, dv
+
+
+def decode_workspace_bytes(params: Params, n_q: int) -> int:
+    n = load().attn_decode_workspace_bytes(ctypes.byref(params), int(n_q))
+    if n == 0:
+        _raise(1)
+    return int(n)
+
+
+def attn_decode(q, k_cache, v_cache, q_positions=None, theta=0.0, causal=True, scale=0.0, out=None, lse=None,
+                workspace=None):
+    """Decode attention of the n_q query rows q (bf16 [B,H,n_q,D], un-rotated;
+    row r is the token at sequence index S - n_q + r) against the cache
+    (k_cache rotated, v_cache; bf16 [B,H,S,D]).  Returns (o bf16 [B,H,n_q,D],
+    lse fp32 [B,H,n_q])."""
+    import torch
+
+    _check_bhsd("q", q)
+    B, H, nq, D = q.shape
+    _check_bhsd("k_cache", k_cache)
+    S = k_cache.shape[2]
+    _check_bhsd("k_cache", k_cache, (B, H, S, D))
+    _check_bhsd("v_cache", v_cache, (B, H, S, D))
+    _check_bs("q_positions", q_positions, B, nq)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, nq), dtype=torch.float32, device=q.device)
+    _check_bhsd("out", out, q.shape)
+    p = make_params(B, H, S, D, theta=theta, causal=causal, scale=scale)
+    need = decode_workspace_bytes(p, nq)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    _raise(load().attn_decode(ctypes.byref(p), int(nq), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(q_positions),
+                              _ptr(out), _ptr(lse), _ptr(workspace), nbytes, _stream()))
+    return out, lse

@@ -2,6 +2,7 @@
 // and the launch sequence of each operation.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -227,6 +228,43 @@ int prepare(const attn_params* p, const Plan& pl, const void* q, const void* k, 
   return ATTN_OK;
 }
 
+// Decode workspace: rotated query rows, then the chunk states.  About 2048
+// waves (8 per CU) keep enough K/V bytes in flight to cover HBM latency; a
+// chunk has at least 256 keys and a multiple of kDecodeTile.
+struct DecodePlan {
+  int n_chunks, chunk;
+  size_t off_qr, off_po, off_ml, total;
+};
+
+DecodePlan make_decode_plan(const attn_params* p, int n_q) {
+  DecodePlan d{};
+  const int64_t bh = (int64_t)p->batch * p->heads;
+  const int S = p->seqlen;
+  int64_t want = std::max<int64_t>(1, (2048 + bh - 1) / bh);
+  int64_t most = std::max(1, (S + 255) / 256);
+  int64_t n = std::min(want, most);
+  int64_t chunk = (S + n - 1) / n;
+  chunk = (chunk + kDecodeTile - 1) / kDecodeTile * kDecodeTile;
+  d.chunk = (int)chunk;
+  d.n_chunks = (int)((S + chunk - 1) / chunk);
+  size_t off = 0;
+  d.off_qr = off;
+  if (p->rope_theta > 0.0) off += align256((size_t)bh * n_q * p->head_dim * 2);
+  d.off_po = off;
+  off += align256((size_t)bh * d.n_chunks * n_q * p->head_dim * 4);
+  d.off_ml = off;
+  off += align256((size_t)bh * d.n_chunks * n_q * 2 * 4);
+  d.total = off;
+  return d;
+}
+
+int check_decode_rows(int32_t n_q, int S) {
+  if (n_q < 1 || n_q > kDecodeMaxRows)
+    return fail(ATTN_ERR_INVALID_ARG, "n_q %d must be in [1, %d]", n_q, kDecodeMaxRows);
+  if (n_q > S) return fail(ATTN_ERR_INVALID_ARG, "n_q %d larger than the cache length %d", n_q, S);
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -412,6 +450,76 @@ int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v, 
   rc = hip_status(timed_launch(ATTN_KERNEL_BWD_DQ, st, [&] { return launch_attn_bwd_dq(a, pl.D, st); }), "attn_bwd dq launch");
   if (rc) return rc;
   rc = hip_status(timed_launch(ATTN_KERNEL_BWD_DKDV, st, [&] { return launch_attn_bwd_dkdv(a, pl.D, st); }), "attn_bwd dkdv launch");
+  if (rc) return rc;
+  g_err[0] = 0;
+  return ATTN_OK;
+}
+
+size_t attn_decode_workspace_bytes(const attn_params* p, int32_t n_q) {
+  if (check_params(p) != ATTN_OK) return 0;
+  if (check_decode_rows(n_q, p->seqlen) != ATTN_OK) return 0;
+  g_err[0] = 0;
+  return make_decode_plan(p, n_q).total;
+}
+
+int attn_decode(const attn_params* p, int32_t n_q, const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* q_positions, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  int rc = check_params(p);
+  if (rc) return rc;
+  rc = check_decode_rows(n_q, p->seqlen);
+  if (rc) return rc;
+  if (!q || !k_cache || !v_cache || !o || !lse)
+    return fail(ATTN_ERR_INVALID_ARG, "q, k_cache, v_cache, o and lse must not be NULL");
+  const void* ptrs[] = {q, k_cache, v_cache, q_positions, o, lse, workspace};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return fail(ATTN_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  DecodePlan dp = make_decode_plan(p, n_q);
+  if (workspace == nullptr || workspace_bytes < dp.total)
+    return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", dp.total, workspace_bytes,
+                workspace ? "" : " (NULL)");
+  rc = check_device();
+  if (rc) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const bool rope = p->rope_theta > 0.0;
+  if (rope) {
+    RopeArgs r{};
+    r.x = (const uint16_t*)q;
+    r.y = (uint16_t*)(ws + dp.off_qr);
+    r.pos = q_positions;
+    r.pos_base = p->seqlen - n_q;
+    r.B = p->batch;
+    r.H = p->heads;
+    r.S = n_q;
+    r.D = p->head_dim;
+    r.inverse = 0;
+    fill_turns(r.turns, p->head_dim, p->rope_theta);
+    rc = hip_status(timed_launch(ATTN_KERNEL_ROPE, st, [&] { return launch_rope(r, st); }), "rope(q) launch");
+    if (rc) return rc;
+  }
+  DecodeArgs a{};
+  a.q = rope ? (const uint16_t*)(ws + dp.off_qr) : (const uint16_t*)q;
+  a.k = (const uint16_t*)k_cache;
+  a.v = (const uint16_t*)v_cache;
+  a.part_o = (float*)(ws + dp.off_po);
+  a.part_ml = (float*)(ws + dp.off_ml);
+  a.o = (uint16_t*)o;
+  a.lse = lse;
+  a.B = p->batch;
+  a.H = p->heads;
+  a.S = p->seqlen;
+  a.n_q = n_q;
+  a.n_chunks = dp.n_chunks;
+  a.chunk = dp.chunk;
+  a.scale_log2 = scale_of(p) * 1.4426950408889634f;
+  a.causal = p->causal;
+  rc = hip_status(timed_launch(ATTN_KERNEL_DECODE, st, [&] { return launch_attn_decode_partial(a, p->head_dim, st); }),
+                  "attn_decode partial launch");
+  if (rc) return rc;
+  rc = hip_status(
+      timed_launch(ATTN_KERNEL_DECODE_MERGE, st, [&] { return launch_attn_decode_combine(a, p->head_dim, st); }),
+      "attn_decode merge launch");
   if (rc) return rc;
   g_err[0] = 0;
   return ATTN_OK;

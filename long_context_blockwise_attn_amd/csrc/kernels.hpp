@@ -15,7 +15,8 @@ constexpr int kSegBlock = 32;     // rows per segment-range block
 struct RopeArgs {
   const uint16_t* x;
   uint16_t* y;
-  const int32_t* pos;  // [B,S] or null (pos = s)
+  const int32_t* pos;  // [B,S] or null (pos = pos_base + s)
+  int pos_base;
   int B, H, S, D;
   int inverse;
   double turns[64];  // theta^(-2i/D) / (2 pi), i < D/2
@@ -92,6 +93,26 @@ struct BwdArgs {
   double turns[64];
 };
 
+// Decode (split-K): one wave per chunk of `chunk` keys of one (b,h) keeps
+// the online-softmax state of n_q <= 32 query rows; a second kernel merges
+// the chunks.
+constexpr int kDecodeTile = 32;     // keys per decode tile
+constexpr int kDecodeMaxRows = 32;  // query rows per (b,h) in one decode call
+
+struct DecodeArgs {
+  const uint16_t* q;  // rotated query rows [B,H,n_q,D]
+  const uint16_t* k;  // key cache [B,H,S,D] (rotated by the caller)
+  const uint16_t* v;  // value cache [B,H,S,D]
+  float* part_o;      // [B,H,n_chunks,n_q,D] unnormalised partial outputs
+  float* part_ml;     // [B,H,n_chunks,n_q,2] (m in log2 units of the scaled scores, l)
+  uint16_t* o;        // [B,H,n_q,D]
+  float* lse;         // [B,H,n_q], natural log
+  int B, H, S, n_q;
+  int n_chunks, chunk;  // chunk: keys per chunk, a multiple of kDecodeTile
+  float scale_log2;
+  int causal;
+};
+
 hipError_t launch_rope(const RopeArgs& a, hipStream_t st);
 hipError_t launch_transpose(const TransposeArgs& a, hipStream_t st);
 hipError_t launch_block_ranges(const int32_t* seg, int B, int S, int nblk, int2* out, hipStream_t st);
@@ -99,5 +120,7 @@ hipError_t launch_tile_ranges(const TileRangeArgs& a, hipStream_t st);
 hipError_t launch_attn_fwd(const FwdArgs& a, int D, hipStream_t st);
 hipError_t launch_attn_bwd_dq(const BwdArgs& a, int D, hipStream_t st);
 hipError_t launch_attn_bwd_dkdv(const BwdArgs& a, int D, hipStream_t st);
+hipError_t launch_attn_decode_partial(const DecodeArgs& a, int D, hipStream_t st);
+hipError_t launch_attn_decode_combine(const DecodeArgs& a, int D, hipStream_t st);
 
 }  // namespace bwattn

@@ -27,7 +27,7 @@ __global__ void rope_kernel(RopeArgs a) {
   int64_t bs = tid / groups;
   int s = (int)(bs % a.S);
   int b = (int)(bs / a.S);
-  double pos = a.pos ? (double)a.pos[bs] : (double)s;
+  double pos = a.pos ? (double)a.pos[bs] : (double)(a.pos_base + s);
   float c[4], sn[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {

@@ -28,6 +28,10 @@ video_text_256k
 full_1m
     B1 H32 D128 S1048576, theta 5e7 (the 1M stage); one document; causal; the
     sequence is cut into 64 chunks of 16384 and K/V are visited in ring order.
+decode_1m
+    B1 H32 D128, a cache of S = 1048576 keys and values, theta 5e7, and n_q = 1
+    new query row per (b,h) (token-by-token generation at 1M context); bf16
+    N(0,1) q [B,H,n_q,D], k, v [B,H,S,D]; causal.
 """
 from __future__ import annotations
 
@@ -68,6 +72,7 @@ WORKLOADS = {
     "video_text_256k": Workload("video_text_256k", 1, 32, 128, 262144, 1e7, packing="video_text",
                                 backward=False, seed=4),
     "full_1m": Workload("full_1m", 1, 32, 128, 1048576, 5e7, kv_chunk=16384, seed=5),
+    "decode_1m": Workload("decode_1m", 1, 32, 128, 1048576, 5e7, backward=False, seed=6, extra={"n_q": 1}),
 }
 
 

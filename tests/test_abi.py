@@ -29,7 +29,8 @@ def declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert {"attn_fwd", "attn_bwd", "rope_apply", "attn_workspace_bytes", "attn_status_string",
-            "attn_last_error", "attn_profile_events", "attn_profile_count"} <= set(names)
+            "attn_last_error", "attn_profile_events", "attn_profile_count", "attn_decode",
+            "attn_decode_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -102,3 +103,46 @@ def test_profile_hook_arguments(lib):
     assert lib.attn_profile_events(1, None, None, 0) == 0
     assert lib.attn_profile_count(1) == 0
     assert lib.attn_profile_count(17) == -1
+
+
+def test_decode_argument_errors_before_any_hip_call(lib):
+    import long_context_blockwise_attn_amd as bw
+
+    V = ctypes.c_void_p
+    p = bw.make_params(1, 2, 4096, 128, theta=1e6)
+
+    def call(n_q=4, q=16, k=32, v=48, pos=None, o=64, lse=80, ws=None, nbytes=0, params=p):
+        return lib.attn_decode(ctypes.byref(params), n_q, V(q) if q else None, V(k) if k else None,
+                               V(v) if v else None, V(pos) if pos else None, V(o) if o else None,
+                               V(lse) if lse else None, V(ws) if ws else None, nbytes, None)
+
+    assert call(n_q=0) == 1 and b"n_q" in lib.attn_last_error()
+    assert call(n_q=33) == 1
+    assert call(n_q=5, params=bw.make_params(1, 2, 4, 128)) == 1  # more rows than cached keys
+    assert call(q=0) == 1
+    assert call(k=40) == 1 and b"aligned" in lib.attn_last_error()
+    assert call(params=bw.make_params(1, 2, 4096, 96)) == 2
+    assert call() == 3  # no workspace
+    assert call(ws=4096, nbytes=16) == 3
+    assert lib.attn_decode_workspace_bytes(ctypes.byref(p), 0) == 0
+    n1 = bw.decode_workspace_bytes(p, 1)
+    n32 = bw.decode_workspace_bytes(p, 32)
+    assert 0 < n1 < n32
+
+
+def test_decode_split_is_chunks_of_tiles(lib):
+    """The workspace holds one partial state per chunk and row: its size pins
+    the chunk count the plan chose (about 2048 chunks in all, at least 256
+    keys each)."""
+    import long_context_blockwise_attn_amd as bw
+
+    for B, H, S in ((1, 32, 1 << 20), (1, 2, 1000), (2, 1, 300), (1, 32, 32)):
+        p = bw.make_params(B, H, S, 128, theta=0.0)
+        n = bw.decode_workspace_bytes(p, 1)
+        # no rotated-q block without RoPE: partial O (D floats) + (m, l), each 256-byte aligned
+        per_chunk_o, per_chunk_ml = B * H * 128 * 4, B * H * 2 * 4
+        al = lambda x: (x + 255) // 256 * 256
+        want = min(max(1, -(-2048 // (B * H))), max(1, -(-S // 256)))
+        chunk = -(-(-(-S // want)) // 32) * 32
+        nc = -(-S // chunk)
+        assert n == al(nc * per_chunk_o) + al(nc * per_chunk_ml), (B, H, S, n, nc)

@@ -1,0 +1,109 @@
+"""attn_decode on the GPU against the oracle: the n_q query rows at the end of
+a sequence attend to the whole key/value cache (exact attention; zhao9797
+page, 模型架构), so the oracle's forward on those rows is the answer.  The
+cache holds keys rotated with rope_apply; the oracle rotates the raw keys
+itself."""
+import numpy as np
+import pytest
+
+from helpers import assert_parity, to64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def run_decode(oracle, torch, B, H, S, D, nq, causal, theta, seed, pos_offset=0, explicit_positions=False):
+    import long_context_blockwise_attn_amd as bw
+    from long_context_blockwise_attn_amd.inputs import random_case
+
+    (q, k, v, _), _, pos = random_case(B, H, S, D, seed)
+    pos = pos + pos_offset
+    print("decode B%d H%d S%d D%d n_q %d causal %d theta %g pos+%d" % (B, H, S, D, nq, causal, theta, pos_offset),
+          flush=True)
+    dpos = torch.from_numpy(pos).cuda()
+    kc, vc = k.cuda(), v.cuda()
+    kcache = bw.rope_apply(kc, dpos, theta=theta) if theta > 0 else kc
+    qd = q[:, :, S - nq:].contiguous().cuda()
+    qpos = dpos[:, S - nq:].contiguous() if (explicit_positions or pos_offset) else None
+    o, lse = bw.attn_decode(qd, kcache, vc, qpos, theta=theta, causal=causal)
+    torch.cuda.synchronize()
+    rows = np.arange(S - nq, S, dtype=np.int64)
+    ro, rlse = oracle.attn_fwd(to64(q), to64(k), to64(v), None, pos, theta=theta, causal=causal, rows=rows)
+    eo = assert_parity(to64(o), ro, "O")
+    el = assert_parity(lse.cpu().numpy(), rlse, "LSE")
+    print("  (max, mean) abs errors O %s LSE %s" % (eo, el), flush=True)
+    return o, lse
+
+
+@pytest.mark.parametrize("B,H,S,D,nq,causal,theta", [
+    (2, 3, 1000, 128, 1, True, 1e6),     # one new token
+    (1, 2, 777, 64, 5, True, 1e4),       # D = 64, ragged tail
+    (1, 2, 4097, 128, 32, True, 5e7),    # a full row group, tail of one key
+    (1, 2, 300, 128, 3, False, 0.0),     # no causal term, no RoPE
+    (1, 1, 33, 128, 32, True, 1e6),      # nearly every key is new
+    (1, 2, 1, 128, 1, True, 1e6),        # a single cached key
+    (1, 2, 100000, 128, 8, True, 1e7),   # hundreds of chunks
+])
+def test_decode_matches_oracle(oracle, torch_cuda, B, H, S, D, nq, causal, theta):
+    run_decode(oracle, torch_cuda, B, H, S, D, nq, causal, theta, seed=S + nq)
+
+
+def test_decode_explicit_positions(oracle, torch_cuda):
+    run_decode(oracle, torch_cuda, 1, 2, 2000, 128, 4, True, 1e6, seed=11, pos_offset=12345)
+
+
+def test_decode_equals_forward_last_rows(torch_cuda):
+    """The split-K merge reaches the forward's result for the same rows (to
+    rounding: the two sum in different orders)."""
+    import long_context_blockwise_attn_amd as bw
+
+    torch = torch_cuda
+    g = torch.Generator(device="cuda").manual_seed(5)
+    B, H, S, D, nq = 1, 4, 9000, 128, 16
+    q, k, v = (torch.randn(B, H, S, D, generator=g, device="cuda").to(torch.bfloat16) for _ in range(3))
+    o_f, lse_f = bw.attn_fwd(q, k, v, None, None, theta=1e6)
+    kc = bw.rope_apply(k, None, theta=1e6)
+    o_d, lse_d = bw.attn_decode(q[:, :, S - nq:].contiguous(), kc, v, None, theta=1e6)
+    torch.cuda.synchronize()
+    assert_parity(to64(o_d), to64(o_f[:, :, S - nq:]), "O decode vs forward", max_abs=1e-2, mean_abs=1e-3)
+    assert_parity(lse_d.cpu().numpy(), lse_f[:, :, S - nq:].cpu().numpy(), "LSE decode vs forward",
+                  max_abs=1e-3, mean_abs=1e-4)
+
+
+def test_decode_full_1m(oracle, torch_cuda):
+    """The 1M-key cache of the decode workload (32 heads), with 4 new rows
+    instead of its one: two heads checked against the oracle."""
+    import long_context_blockwise_attn_amd as bw
+    from long_context_blockwise_attn_amd.inputs import WORKLOADS, randn_bf16
+
+    torch = torch_cuda
+    w = WORKLOADS["decode_1m"]
+    B, H, S, D, nq = w.batch, w.heads, w.seqlen, w.head_dim, 4
+    q = randn_bf16((B, H, nq, D), w.seed * 16, "cuda")
+    k = randn_bf16((B, H, S, D), w.seed * 16 + 1, "cuda")
+    v = randn_bf16((B, H, S, D), w.seed * 16 + 2, "cuda")
+    print("decode_1m: B%d H%d S%d D%d n_q %d theta %g" % (B, H, S, D, nq, w.theta), flush=True)
+    kc = bw.rope_apply(k, None, theta=w.theta)
+    o, lse = bw.attn_decode(q, kc, v, None, theta=w.theta)
+    torch.cuda.synchronize()
+    del kc
+    rows = np.arange(S - nq, S, dtype=np.int64)
+    pos = np.arange(S, dtype=np.int32)[None]
+    for h in (0, 29):
+        qh = np.zeros((1, 1, S, D))
+        qh[0, 0, S - nq:] = to64(q[:, h])[0]
+        ro, rlse = oracle.attn_fwd(qh, to64(k[:, h:h + 1]), to64(v[:, h:h + 1]), None, pos, theta=w.theta,
+                                   causal=True, rows=rows)
+        eo = assert_parity(to64(o[:, h:h + 1]), ro, "O h%d" % h)
+        el = assert_parity(lse[:, h:h + 1].cpu().numpy(), rlse, "LSE h%d" % h)
+        print("  head %d: (max, mean) abs errors O %s LSE %s" % (h, eo, el), flush=True)
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
