@@ -32,7 +32,8 @@ METRIC = "causal attention TFLOP/s fwd+bwd (32h×d128, S=32K–1M) and % of bf16
 # MI355X dense bf16 MFMA peak: 256 CUs x 4 SIMDs x 1024 FLOP/clk x 2.4 GHz (the 2.5 PFLOP/s figure)
 BF16_PEAK_TFLOPS = 2516.6
 HBM_PEAK_GBS = 8000.0
-KERNELS = {"rope": 0, "fwd": 1, "bwd_dq": 2, "bwd_dkdv": 3}
+KERNELS = {"rope": 0, "fwd": 1, "bwd_dq": 2, "bwd_dkdv": 3, "decode": 4, "decode_merge": 5}
+DECODE_METRIC = "decode attention HBM GB/s (1M-token KV cache, 32h×d128, one new row) and % of HBM peak"
 
 
 def visible_pairs(lengths, causal=True):
@@ -86,7 +87,8 @@ def cpu_baseline(w, q, k, v, do, seg, pos, budget_s):
 
 
 # rocprofv3 kernel-name fragments of the timed kernels
-KERNEL_SYMBOLS = {"fwd": "attn_fwd_kernel", "bwd_dq": "attn_bwd_dq_kernel", "bwd_dkdv": "attn_bwd_dkdv_kernel"}
+KERNEL_SYMBOLS = {"fwd": "attn_fwd_kernel", "bwd_dq": "attn_bwd_dq_kernel", "bwd_dkdv": "attn_bwd_dkdv_kernel",
+                  "decode": "attn_decode_partial_kernel"}
 
 
 def kernel_source_hash():
@@ -165,13 +167,139 @@ def load_traffic(workload, kernel):
     return None if k is None else k.get("traffic_bytes")
 
 
+def event_arrays(lib, torch, names, n_each):
+    """Ask the library to bracket the next n_each[name] launches of each
+    kernel with HIP events on the launch stream."""
+    ev, keep = {}, []
+    for name in names:
+        n = n_each[name]
+        st = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        sp = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in st + sp:
+            e.record()  # torch creates the underlying HIP event on first record
+        torch.cuda.synchronize()
+        arr_t = (ctypes.c_void_p * n)(*[e.cuda_event for e in st])
+        arr_p = (ctypes.c_void_p * n)(*[e.cuda_event for e in sp])
+        keep += [arr_t, arr_p]
+        assert lib.attn_profile_events(KERNELS[name], arr_t, arr_p, n) == 0
+        ev[name] = (st, sp)
+    return ev, keep
+
+
+def decode_bench(args, w):
+    """One step = one attn_decode call: the n_q new rows of every (b,h)
+    against the whole cache (keys already rotated, as a cache holds them).
+    Throughput = algorithmic bytes (the K and V cache read once, q and o) per
+    second; the path is bound by HBM."""
+    import torch
+
+    import long_context_blockwise_attn_amd as bw
+    from long_context_blockwise_attn_amd.inputs import randn_bf16
+
+    dev = torch.device("cuda:0")
+    B, H, S, D, nq = w.batch, w.heads, w.seqlen, w.head_dim, w.extra["n_q"]
+    q = randn_bf16((B, H, nq, D), w.seed * 16, dev)
+    k = randn_bf16((B, H, S, D), w.seed * 16 + 1, dev)
+    v = randn_bf16((B, H, S, D), w.seed * 16 + 2, dev)
+    kc = bw.rope_apply(k, None, theta=w.theta)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, nq), dtype=torch.float32, device=dev)
+    p = bw.make_params(B, H, S, D, theta=w.theta, causal=w.causal)
+    ws = torch.empty(bw.decode_workspace_bytes(p, nq), dtype=torch.uint8, device=dev)
+
+    def step():
+        bw.attn_decode(q, kc, v, None, theta=w.theta, causal=w.causal, out=o, lse=lse, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    lib = bw.load()
+    ev, keep = event_arrays(lib, torch, ["decode", "decode_merge"], {"decode": args.steps, "decode_merge": args.steps})
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    kernel_ms = {}
+    for name, (st, sp) in ev.items():
+        cnt = lib.attn_profile_count(KERNELS[name])
+        kernel_ms[name] = float(np.mean([a.elapsed_time(b) for a, b in zip(st[:cnt], sp[:cnt])]))
+        lib.attn_profile_events(KERNELS[name], None, None, 0)
+
+    cache_bytes = 2.0 * B * H * S * D * 2
+    step_bytes = cache_bytes + 2.0 * B * H * nq * D * 2 + B * H * nq * 4
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    part_bytes = cache_bytes + B * H * nq * D * 2  # the partial kernel reads the cache and the rotated rows
+    part_gbs = part_bytes / (kernel_ms["decode"] * 1e-3) / 1e9
+    roofline = {"kernel": "decode", "bound": "hbm", "achieved": part_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": part_gbs / HBM_PEAK_GBS, "traffic": load_traffic(w.name, "decode"),
+                "traffic_unit": "HBM bytes per launch", "bytes_per_launch": part_bytes}
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        bcopy = torch.empty_like(a)
+        bcopy.copy_(a)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        oracle.build(force=False)
+        rows = np.arange(S - nq, S, dtype=np.int64)
+        qh = np.zeros((1, 1, S, D))
+        qh[0, 0, S - nq:] = q[:1, :1].float().cpu().numpy()[0, 0]
+        kh = k[:1, :1].float().cpu().numpy().astype(np.float64)
+        vh = v[:1, :1].float().cpu().numpy().astype(np.float64)
+        reps, dt = 0, 0.0
+        t_start = time.perf_counter()
+        while dt < 0.5 * args.cpu_seconds or reps == 0:
+            oracle.attn_fwd(qh, kh, vh, None, None, theta=w.theta, causal=w.causal, rows=rows)
+            reps += 1
+            dt = time.perf_counter() - t_start
+        head_bytes = 2.0 * S * D * 2 + 2.0 * nq * D * 2 + nq * 4
+        cpu = {"value": reps * head_bytes / dt / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
+               "kind": "oracle",
+               "sample": "%d oracle calls on head 0 of %d (the n_q rows against its whole cache, K rotated inside), "
+                         "%.1f s; credited that head's bf16 cache bytes per call" % (reps, H, dt),
+               "seconds": dt}
+
+    out = {
+        "metric": DECODE_METRIC,
+        "value": gbs,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "heads": H, "head_dim": D, "cache_len": S, "n_q": nq,
+                   "rope_theta": w.theta, "mask": "causal" if w.causal else "none", "parallelism": "single GPU"},
+        "pct_of_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS,
+        "kernels_ms": {n: round(t, 4) for n, t in kernel_ms.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    del keep
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama7b_32k",
-                    help="llama7b_32k (default), packing_128k, video_text_256k, full_1m, tiny")
+                    help="llama7b_32k (default), packing_128k, video_text_256k, full_1m, tiny, "
+                         "decode_1m (attn_decode; HBM GB/s)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=24.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -203,6 +331,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = WORKLOADS[args.workload]
+    if "n_q" in w.extra:
+        decode_bench(args, w)
+        return
     B, H, S, D = w.batch, w.heads, w.seqlen, w.head_dim
     seg_np, pos_np, lengths = packing(w)
     w.extra["lengths"] = lengths
