@@ -17,8 +17,9 @@
 //  - dK/dV kernel: a workgroup owns kBwdBlockK keys and streams Q/dO tiles of
 //    64 rows.  4 contractions per tile pair (S, dP, dV, dK).
 // Operands with k along the sequence (K^T for dQ, Q^T and dO^T for dK/dV)
-// come from transposed copies made by a pre-pass, so every MFMA operand is a
-// 16-byte LDS read.
+// are read from the same row tiles with transposing LDS reads
+// (PTile::read_tr), so each tile is loaded once and no transposed copy is
+// made.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "tile.hpp"
@@ -59,8 +60,8 @@ __device__ __forceinline__ void store_rows(uint16_t* dst_row, const f32x16 (&x)[
 }
 
 // ---------------------------------------------------------------------------
-// dQ (and Delta): NW waves x 32 query rows; tiles of 64 keys of K, V and the
-// transposed K in LDS.  Per 32-key half: S^T = K Q^T and dP^T = V dO^T
+// dQ (and Delta): NW waves x 32 query rows; tiles of 64 keys of K and V in
+// LDS.  Per 32-key half: S^T = K Q^T and dP^T = V dO^T
 // (lane = query row), then dS^T = P^T (dP^T - Delta) and dQ^T += K^T dS^T.
 // ---------------------------------------------------------------------------
 template <int D, int NW, int NSTAGE>
@@ -68,11 +69,10 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
   constexpr int BQ = kFwdBlockQ, BK = kFwdBlockK;
   static_assert(BQ == NW * 32, "one 32-row group per wave");
   constexpr int NDC = D / 16, NDG = D / 32;
-  using KT = PTile<BK, D / 8>;   // K and V rows
-  using KTT = PTile<D, BK / 8>;  // K^T rows (d), 64 keys each
-  constexpr int SEG_OFF = 2 * KT::kBytes + KTT::kBytes;  // segment ids of the tile's keys
+  using KT = PTile<BK, D / 8, 2>;  // K and V rows (K^T read transposed)
+  constexpr int SEG_OFF = 2 * KT::kBytes;  // segment ids of the tile's keys
   constexpr int BUF = SEG_OFF + 256;
-  // ring of [K, V, K^T, seg] stages (see run_pipeline)
+  // ring of [K, V, seg] stages (see run_pipeline)
   __shared__ __attribute__((aligned(16))) char smem[NSTAGE * BUF];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -145,19 +145,15 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
   const float sl2 = a.scale_log2;
   const uint16_t* kh = a.k + base;
   const uint16_t* vh = a.v + base;
-  const uint16_t* kth = a.kt + (int64_t)bh * D * a.sp;
-  TileFill<BK, D / 8, NW> rfill;  // K and V rows
-  TileFill<D, BK / 8, NW> tfill;  // K^T rows
+  TileFill<BK, D / 8, NW, 2> rfill;  // K and V rows
   rfill.init(D * 2, tid);
-  tfill.init(a.sp * 2, tid);
   auto load = [&](int t, char* buf) {
     const uint32_t rbytes = (uint32_t)(S - t * BK) * D * 2;
     rfill.fill(kh + (int64_t)t * BK * D, rbytes, buf);
     rfill.fill(vh + (int64_t)t * BK * D, rbytes, buf + KT::kBytes);
-    tfill.fill(kth + t * BK, (uint32_t)(D * a.sp - t * BK) * 2, buf + 2 * KT::kBytes);
     if (use_seg && w == 0) row64_to_lds(segb, t * BK, S, buf + SEG_OFF, lane);
   };
-  const int per_tile = 2 * rfill.count() + tfill.count() + (use_seg && w == 0 ? 1 : 0);
+  const int per_tile = 2 * rfill.count() + (use_seg && w == 0 ? 1 : 0);
   auto compute = [&](int t, const char* buf) {
     const int k0 = t * BK;
     bool skip = q0 >= S || (a.causal && k0 > qlast);
@@ -172,7 +168,6 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
     if (!skip) {
       const char* ktl = buf;
       const char* vtl = buf + KT::kBytes;
-      const char* kttl = buf + 2 * KT::kBytes;
       const int* segk_lds = (const int*)(buf + SEG_OFF);
       const bool need_mask = seg_mask || (k0 + BK > S) || (a.causal && k0 + BK - 1 > q0);
 #pragma unroll
@@ -209,8 +204,11 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
                                                     pack_bf16x2(s[r0 + 4], s[r0 + 5]), pack_bf16x2(s[r0 + 6], s[r0 + 7])});
         }
         // dQ^T += K^T dS^T over the 32 keys of this half
-        lds_mfma_pipe<2 * NDG, 6>([&](int i) { return KTT::read(kttl, 32 * (i % NDG), 2 * kg + i / NDG, lane); },
-                                  [&](int i, bf16x8 x) { dq[i % NDG] = mfma32(x, dsk[i / NDG], dq[i % NDG]); });
+        // K^T operands straight from the K rows: keys 32 kg + 16 c .. in the
+        // order dsk[c] holds them
+        lds_mfma_pipe<2 * NDG, 6>(
+            [&](int i) { return KT::read_tr(ktl, 32 * kg + 16 * (i / NDG), 32 * (i % NDG), lane); },
+            [&](int i, bf16x8 x) { dq[i % NDG] = mfma32(x, dsk[i / NDG], dq[i % NDG]); });
       }
     }
   };
@@ -226,8 +224,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dK/dV: NW waves x 32 keys; tiles of 64 query rows of Q, dO and their
-// transposed copies in LDS.  Scores are kept with lane = key: S = Q K^T and
+// dK/dV: NW waves x 32 keys; tiles of 64 query rows of Q and dO in LDS.  Scores are kept with lane = key: S = Q K^T and
 // dP = dO V^T (K and V rows of the lane's key stay in registers), then
 // dV^T += dO^T P and dK^T += Q^T dS.
 // ---------------------------------------------------------------------------
@@ -236,11 +233,10 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
   constexpr int BKV = kBwdBlockK, BQT = kBwdBlockQ;
   static_assert(BKV == NW * 32, "one 32-key group per wave");
   constexpr int NDC = D / 16, NDG = D / 32;
-  using QT = PTile<BQT, D / 8>;   // Q and dO rows
-  using QTT = PTile<D, BQT / 8>;  // Q^T and dO^T rows (d), 64 query rows each
-  constexpr int SB = 2 * QT::kBytes + 2 * QTT::kBytes;  // row statistics: -LSE log2e [64], -Delta [64], seg [64]
+  using QT = PTile<BQT, D / 8, 2>;  // Q and dO rows (Q^T, dO^T read transposed)
+  constexpr int SB = 2 * QT::kBytes;  // row statistics: -LSE log2e [64], -Delta [64], seg [64]
   constexpr int BUF = SB + 3 * 256;
-  // ring of [Q, dO, Q^T, dO^T, statistics] stages (see run_pipeline)
+  // ring of [Q, dO, statistics] stages (see run_pipeline)
   __shared__ __attribute__((aligned(16))) char smem[NSTAGE * BUF];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -302,31 +298,24 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
   const float sl2 = a.scale_log2;
   const uint16_t* qh = a.q + base;
   const uint16_t* dh = a.dout + base;
-  const uint16_t* qth = a.qt + (int64_t)bh * D * a.sp;
-  const uint16_t* dth = a.dot + (int64_t)bh * D * a.sp;
   const float* nlse_h = a.nlse2 + (int64_t)bh * S;
   const float* ndel_h = a.ndelta + (int64_t)bh * S;
 
   // tiles of a Q block and its row statistics (-LSE log2(e), -Delta,
   // segment id), the statistics fetched by wave 0
-  TileFill<BQT, D / 8, NW> rfill;  // Q and dO rows
-  TileFill<D, BQT / 8, NW> tfill;  // Q^T and dO^T rows
+  TileFill<BQT, D / 8, NW, 2> rfill;  // Q and dO rows
   rfill.init(D * 2, tid);
-  tfill.init(a.sp * 2, tid);
   auto load = [&](int t, char* buf) {
     const uint32_t rbytes = (uint32_t)(S - t * BQT) * D * 2;
-    const uint32_t tbytes = (uint32_t)(D * a.sp - t * BQT) * 2;
     rfill.fill(qh + (int64_t)t * BQT * D, rbytes, buf);
     rfill.fill(dh + (int64_t)t * BQT * D, rbytes, buf + QT::kBytes);
-    tfill.fill(qth + t * BQT, tbytes, buf + 2 * QT::kBytes);
-    tfill.fill(dth + t * BQT, tbytes, buf + 2 * QT::kBytes + QTT::kBytes);
     if (w == 0) {
       row64_to_lds(nlse_h, t * BQT, S, buf + SB, lane);
       row64_to_lds(ndel_h, t * BQT, S, buf + SB + 256, lane);
       if (use_seg) row64_to_lds(segb, t * BQT, S, buf + SB + 512, lane);
     }
   };
-  const int per_tile = 2 * rfill.count() + 2 * tfill.count() + (w == 0 ? (use_seg ? 3 : 2) : 0);
+  const int per_tile = 2 * rfill.count() + (w == 0 ? (use_seg ? 3 : 2) : 0);
   auto compute = [&](int t, const char* buf) {
     const int i0 = t * BQT;
     const int ilast = min(S - 1, i0 + BQT - 1);
@@ -342,8 +331,6 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
     if (!skip) {
       const char* qtl = buf;
       const char* dtl = buf + QT::kBytes;
-      const char* qttl = buf + 2 * QT::kBytes;
-      const char* dttl = buf + 2 * QT::kBytes + QTT::kBytes;
       const float* st = (const float*)(buf + SB);
       const bool need_mask = seg_mask || (i0 + BQT > S) || (a.causal && i0 < j0 + 31);
 #pragma unroll
@@ -398,8 +385,10 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
         for (int c = 0; c < 2; ++c) {
 #pragma unroll
           for (int dg = 0; dg < NDG; ++dg) {
-            bf16x8 dta = QTT::read(dttl, 32 * dg, 2 * qg + c, lane);
-            bf16x8 qta = QTT::read(qttl, 32 * dg, 2 * qg + c, lane);
+            // dO^T and Q^T from the row tiles: rows 32 qg + 16 c .. in the
+            // order pk[c] and dsk[c] hold them
+            bf16x8 dta = QT::read_tr(dtl, 32 * qg + 16 * c, 32 * dg, lane);
+            bf16x8 qta = QT::read_tr(qtl, 32 * qg + 16 * c, 32 * dg, lane);
             dv[dg] = mfma32(dta, pk[c], dv[dg]);
             dk[dg] = mfma32(qta, dsk[c], dk[dg]);
           }

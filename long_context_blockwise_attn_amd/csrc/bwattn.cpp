@@ -90,7 +90,7 @@ struct Plan {
   int B, H, S, D, Sp;
   bool rope, seg;
   int nblk, n_qtiles, n_ktiles, n_bkv, n_bq;
-  size_t off_qr, off_kr, off_vt, off_qt, off_kt, off_dot, off_delta, off_blk, off_qrange, off_krange, total;
+  size_t off_qr, off_kr, off_vt, off_delta, off_blk, off_qrange, off_krange, total;
 };
 
 // Workspace layout.  The segment-dependent parts are always reserved so that
@@ -122,12 +122,6 @@ Plan make_plan(const attn_params* p, int which) {
     off += align256(nt * 2);
   }
   if (which == 1) {
-    pl.off_qt = off;
-    off += align256(nt * 2);
-    pl.off_kt = off;
-    off += align256(nt * 2);
-    pl.off_dot = off;
-    off += align256(nt * 2);
     pl.off_delta = off;  // -Delta, then -LSE log2(e)
     off += 2 * align256((size_t)pl.B * pl.H * pl.S * 4);
   }
@@ -399,26 +393,6 @@ int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v, 
   a.q = pl.rope ? (const uint16_t*)(ws + pl.off_qr) : (const uint16_t*)q;
   a.k = pl.rope ? (const uint16_t*)(ws + pl.off_kr) : (const uint16_t*)k;
   a.v = (const uint16_t*)v;
-  a.qt = (const uint16_t*)(ws + pl.off_qt);
-  a.kt = (const uint16_t*)(ws + pl.off_kt);
-  a.dot = (const uint16_t*)(ws + pl.off_dot);
-  a.sp = pl.Sp;
-  {
-    TransposeArgs ta{};
-    ta.B = pl.B;
-    ta.H = pl.H;
-    ta.S = pl.S;
-    ta.D = pl.D;
-    ta.Sp = pl.Sp;
-    const uint16_t* srcs[3] = {a.q, a.k, (const uint16_t*)d_o};
-    const uint16_t* dsts[3] = {a.qt, a.kt, a.dot};
-    for (int i = 0; i < 3; ++i) {
-      ta.x = srcs[i];
-      ta.y = (uint16_t*)dsts[i];
-      rc = hip_status(launch_transpose(ta, st), "transpose launch");
-      if (rc) return rc;
-    }
-  }
   a.o = (const uint16_t*)o;
   a.dout = (const uint16_t*)d_o;
   a.lse = lse;

@@ -65,10 +65,6 @@ struct BwdArgs {
   const uint16_t* q;   // rotated queries
   const uint16_t* k;   // rotated keys
   const uint16_t* v;
-  const uint16_t* qt;  // transposed copies [B,H,D,Sp] (order as TransposeArgs)
-  const uint16_t* kt;
-  const uint16_t* dot;
-  int sp;
   const uint16_t* o;
   const uint16_t* dout;
   const float* lse;    // natural log

@@ -5,22 +5,44 @@
 
 namespace bwattn {
 
-// An LDS tile of R rows x C 16-byte chunks (8 bf16 each), row-major with one
-// chunk of padding per row.  With a row stride of (C+1)*16 bytes, the 16-byte
-// reads of 16 consecutive rows at one chunk land on 16 distinct 16-byte bank
-// groups (64 banks of 4 bytes), and 8 consecutive rows on 8 distinct groups
-// of a 32-bank layout, so the MFMA operand reads below are conflict-free,
-// and a lane's reads at different chunks differ by immediate offsets.
-template <int R, int C>
+// An LDS tile of R rows x C 16-byte chunks (8 bf16 each), row-major with P
+// chunks of padding per row.  With P = 1 (row stride (C+1)*16 bytes), the
+// 16-byte reads of 16 consecutive rows at one chunk land on 16 distinct
+// 16-byte bank groups (64 banks of 4 bytes), and 8 consecutive rows on 8
+// distinct groups of a 32-bank layout, so the MFMA operand reads below are
+// conflict-free, and a lane's reads at different chunks differ by immediate
+// offsets.  P = 2 keeps that and also spreads the transposing reads of
+// tr_operand over every bank exactly twice (P = 1 hits some four times).
+template <int R, int C, int P = 1>
 struct PTile {
-  static constexpr int kStride = (C + 1) * 16;
+  static constexpr int kChunks = C;
+  static constexpr int kPad = P;
+  static constexpr int kStride = (C + P) * 16;
   static constexpr int kBytes = R * kStride;
-  static constexpr int kBlocks = R * (C + 1) / 64;  // 1 KiB direct-load blocks
-  static_assert((R * (C + 1)) % 64 == 0, "tile must be whole 1 KiB blocks");
+  static constexpr int kBlocks = R * (C + P) / 64;  // 1 KiB direct-load blocks
+  static_assert((R * (C + P)) % 64 == 0, "tile must be whole 1 KiB blocks");
   // MFMA operand whose lane l holds row r0 + (l % 32) at chunk
   // 2 c + (l / 32): a 32x32x16 operand with k along the row.
   __device__ static __forceinline__ bf16x8 read(const char* t, int r0, int c, int lane) {
     return *(const bf16x8*)(t + (r0 + (lane & 31)) * kStride + (2 * c + (lane >> 5)) * 16);
+  }
+  // The transposed operand (k along the rows): lane l holds column
+  // d = d0 + l % 32 of rows r0 + 8 h + 4 (l / 32) + r in element 4 h + r
+  // (h, r < 2, 4) -- the row order in which a 32x32x16 MFMA result holds its
+  // rows, so a score tile packed to bf16 is the other operand as it stands.
+  // Two ds_read_b64_tr_b16: within each 16-lane group g the instruction
+  // hands lane i element r of the 4 elements that lane 4 r + i / 4 addressed,
+  // element i % 4; lane 16 g + s therefore addresses row 4 (g / 2) + s / 4,
+  // column (16 g + 4 (s % 4)) % 32.
+  __device__ static __forceinline__ bf16x8 read_tr(const char* t, int r0, int d0, int lane) {
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    const int g = lane >> 4, s = lane & 15;
+    const char* p = t + (r0 + 4 * (g >> 1) + (s >> 2)) * kStride + (d0 + ((16 * g + 4 * (s & 3)) & 31)) * 2;
+    i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
+    i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p + 8 * kStride));
+    i16x8 x = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, x);
   }
 };
 
@@ -60,15 +82,15 @@ __device__ __forceinline__ void dma_b32(i32x4 rsrc, const char* lds, uint32_t vo
                : "memory", "m0");
 }
 
-// Direct buffer-to-LDS fill of a PTile<R, C>.  Each 64-lane load fills
+// Direct buffer-to-LDS fill of a PTile<R, C, P>.  Each 64-lane load fills
 // 1 KiB of consecutive LDS, so lane i fetches the global chunk that belongs at
 // its LDS position (pad slots fetch a repeat of the row's last chunk).  The NW
 // waves share the kBlocks blocks; a wave's per-lane byte offsets depend only
 // on the lane and the row pitch, so they are formed once (init) and each tile
 // only moves the buffer base.
-template <int R, int C, int NW>
+template <int R, int C, int NW, int P = 1>
 struct TileFill {
-  static constexpr int kBlocks = PTile<R, C>::kBlocks;
+  static constexpr int kBlocks = PTile<R, C, P>::kBlocks;
   static constexpr int kPer = (kBlocks + NW - 1) / NW;
   uint32_t voff[kPer];
   int w;
@@ -78,7 +100,7 @@ struct TileFill {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       int p = (w + NW * i) * 64 + lane;
-      int row = p / (C + 1), c = min(p % (C + 1), C - 1);
+      int row = p / (C + P), c = min(p % (C + P), C - 1);
       voff[i] = row * row_bytes + c * 16;
     }
   }
