@@ -419,7 +419,7 @@ hipError_t launch_attn_bwd_dq(const BwdArgs& a, int D, hipStream_t st) {
 }
 
 hipError_t launch_attn_bwd_dkdv(const BwdArgs& a, int D, hipStream_t st) {
-  constexpr int NW = 8, NSTAGE = 2;
+  constexpr int NW = 8, NSTAGE = 3;
   dim3 grid((unsigned)((int64_t)a.B * a.H * a.n_bkv)), block(NW * 64);
   if (D == 128)
     hipLaunchKernelGGL((attn_bwd_dkdv_kernel<128, NW, NSTAGE>), grid, block, 0, st, a);
