@@ -212,7 +212,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
       }
     }
   };
-  run_pipeline<NSTAGE>(walk, per_tile, smem, BUF, load, compute);
+  run_pipeline<NSTAGE, false>(walk, per_tile, smem, BUF, load, compute);
 
   if (ok) {
     if (a.rope) {
@@ -396,7 +396,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
       }
     }
   };
-  run_pipeline<NSTAGE>(walk, per_tile, smem, BUF, load, compute);
+  run_pipeline<NSTAGE, true>(walk, per_tile, smem, BUF, load, compute);
 
   if (jok) {
     if (a.rope) {

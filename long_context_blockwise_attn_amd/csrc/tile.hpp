@@ -251,16 +251,22 @@ struct TileWalk {
 };
 
 // Software pipeline over the tile walk with an NSTAGE ring of LDS buffers
-// (ring[i] = base + i * stride).  The loads of tile t + NSTAGE - 1 are issued
-// before tile t is computed.  Waits are explicit: `per_tile` is the number of
-// vector-memory instructions this wave issues per load(t, buf) call, and at
-// the end of each step only the tiles after the next one may still be in
-// flight; the barrier then makes every wave's loads visible.
+// (ring[i] = base + i * stride), in one of two orders:
+//  - LATE = false: a wave issues its loads of tile t + NSTAGE - 1 (into the
+//    slot of tile t - 1, free since the last barrier) before computing tile t;
+//  - LATE = true (NSTAGE >= 3): it issues them after computing tile t.  This
+//    lets the waves that finish first feed the load path while the others
+//    still compute, instead of every wave stalling at the top of the step
+//    until the path has taken the burst.
+// Then it waits for its loads of tile t + 1 and meets the others at the
+// barrier.  Waits are explicit: `per_tile` is the number of vector-memory
+// instructions this wave issues per load(t, buf) call.
 //   load(t, buf):    issue the loads of tile t into buf
 //   compute(t, buf): use tile t in buf
-template <int NSTAGE, class Load, class Compute>
+template <int NSTAGE, bool LATE, class Load, class Compute>
 __device__ __forceinline__ void run_pipeline(TileWalk walk, int per_tile, char* base, int stride, Load&& load,
                                              Compute&& compute) {
+  static_assert(NSTAGE >= 2 && (!LATE || NSTAGE >= 3), "the slot of tile t - 1 takes tile t + NSTAGE - 1");
   TileWalk ahead = walk;  // walk position of the newest tile issued
   int issued = 0;         // tiles issued beyond the one being computed
   if (walk.t >= 0) load(uniform(walk.t), base);
@@ -274,16 +280,20 @@ __device__ __forceinline__ void run_pipeline(TileWalk walk, int per_tile, char* 
   wait_vmem_le(issued * per_tile);
   __syncthreads();
   int cur = 0;
+  auto issue_next = [&]() {
+    if (ahead.t >= 0) ahead.next();
+    if (ahead.t >= 0) {
+      const int fill = cur == 0 ? NSTAGE - 1 : cur - 1;
+      load(uniform(ahead.t), base + fill * stride);
+      ++issued;
+    }
+  };
   while (walk.t >= 0) {
     TileWalk nx = walk;
     nx.next();
-    if (ahead.t >= 0) ahead.next();
-    if (ahead.t >= 0) {
-      int fill = cur + NSTAGE - 1;
-      load(uniform(ahead.t), base + (fill >= NSTAGE ? fill - NSTAGE : fill) * stride);
-      ++issued;
-    }
+    if (!LATE) issue_next();
     compute(uniform(walk.t), (const char*)(base + cur * stride));
+    if (LATE) issue_next();
     if (nx.t >= 0) --issued;
     wait_vmem_le(issued * per_tile);
     __syncthreads();
