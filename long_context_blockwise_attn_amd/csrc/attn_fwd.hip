@@ -119,10 +119,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   // S^T of the tile in `buf`: s[kg] holds keys k0 + 32 kg + 8 (r/4) + 4 hl + r%4
   auto scores = [&](const char* buf, f32x16 (&s)[2]) {
     s[0] = s[1] = f32x16{};
-#pragma unroll
-    for (int dc = 0; dc < NDC; ++dc)
-#pragma unroll
-      for (int kg = 0; kg < 2; ++kg) s[kg] = mfma32(KT::read(buf, 32 * kg, dc, lane), qop[dc], s[kg]);
+    lds_mfma_pipe<2 * NDC, 3>([&](int i) { return KT::read(buf, 32 * (i & 1), i >> 1, lane); },
+                              [&](int i, bf16x8 x) { s[i & 1] = mfma32(x, qop[i >> 1], s[i & 1]); });
   };
   // causal / segment / sequence-end mask of tile t (wave-uniform decision)
   auto mask = [&](int t, const char* buf, f32x16 (&s)[2]) {
@@ -195,10 +193,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   };
   auto pv = [&](const char* buf, const bf16x8 (&pk)[4]) {
     const char* vt = buf + KT::kBytes;
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc)
-#pragma unroll
-      for (int dg = 0; dg < NDG; ++dg) o[dg] = mfma32(VT::read(vt, 32 * dg, kc, lane), pk[kc], o[dg]);
+    lds_mfma_pipe<4 * NDG, 3>([&](int i) { return VT::read(vt, 32 * (i % NDG), i / NDG, lane); },
+                              [&](int i, bf16x8 x) { o[i % NDG] = mfma32(x, pk[i / NDG], o[i % NDG]); });
   };
 
   // --- ping-pong pipeline -------------------------------------------------
