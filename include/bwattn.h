@@ -82,9 +82,9 @@ const char* attn_status_string(int status);
 /* Message of the last error returned on the calling thread ("" if none). */
 const char* attn_last_error(void);
 
-/* Bytes of device workspace that attn_fwd (which = 0) or attn_bwd (which = 1)
- * needs for these parameters; 0 if the parameters are invalid.  rope_apply
- * needs none. */
+/* Bytes of device workspace that attn_fwd (which = 0), attn_bwd (1),
+ * attn_fwd_f32 (2) or attn_bwd_f32 (3) needs for these parameters; 0 if the
+ * parameters are invalid.  rope_apply and rope_apply_f32 need none. */
 size_t attn_workspace_bytes(const attn_params* p, int32_t which);
 
 /* RoPE on x (bf16 [B,H,S,D]) into y (same shape; y may equal x): each pair
@@ -117,6 +117,32 @@ int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, 
 int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v, const void* o,
              const float* lse, const void* d_o, const int32_t* segment_ids, const int32_t* positions,
              void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* fp32 variant.  The paper trains and runs its models in full precision      */
+/* (arXiv 2402.08268, training and inference setup); these entry points take  */
+/* the same operation on fp32 tensors and compute it with fp32 matrix         */
+/* instructions (fp32 products and sums; exp2 and the RoPE sine and cosine by */
+/* the hardware's fp32 approximations).  Conventions as above, with every     */
+/* bf16 tensor replaced by fp32 [B,H,S,D] contiguous; lse stays fp32 [B,H,S]. */
+/* ------------------------------------------------------------------------ */
+
+/* rope_apply on fp32 rows (fp32 rotation, fp64 angle). */
+int rope_apply_f32(const attn_params* p, const float* x, float* y, const int32_t* positions, int32_t inverse,
+                   void* stream);
+
+/* attn_fwd on fp32 q, k, v; o fp32 [B,H,S,D].  workspace:
+ * attn_workspace_bytes(p, 2) bytes. */
+int attn_fwd_f32(const attn_params* p, const float* q, const float* k, const float* v, const int32_t* segment_ids,
+                 const int32_t* positions, float* o, float* lse, void* workspace, size_t workspace_bytes,
+                 void* stream);
+
+/* attn_bwd on fp32 tensors: o and lse from attn_fwd_f32 on the same inputs,
+ * d_o fp32; writes fp32 dq, dk, dv.  workspace: attn_workspace_bytes(p, 3)
+ * bytes. */
+int attn_bwd_f32(const attn_params* p, const float* q, const float* k, const float* v, const float* o,
+                 const float* lse, const float* d_o, const int32_t* segment_ids, const int32_t* positions, float* dq,
+                 float* dk, float* dv, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Decode attention against a long key/value cache: the n_q new query rows
  * of each (b, h) against the p->seqlen = S cached keys, as in 1M-token
@@ -156,7 +182,10 @@ typedef enum {
   ATTN_KERNEL_BWD_DKDV = 3,  /* backward: dK and dV                                   */
   ATTN_KERNEL_DECODE = 4,    /* decode: per-chunk partial states (split-K)            */
   ATTN_KERNEL_DECODE_MERGE = 5, /* decode: merge of the chunk states                  */
-  ATTN_KERNEL_COUNT = 6
+  ATTN_KERNEL_FWD_F32 = 6,   /* fp32 forward main kernel                              */
+  ATTN_KERNEL_BWD_DQ_F32 = 7,   /* fp32 backward: dQ and Delta                        */
+  ATTN_KERNEL_BWD_DKDV_F32 = 8, /* fp32 backward: dK and dV                           */
+  ATTN_KERNEL_COUNT = 9
 } attn_kernel_id;
 
 /* Ask the library to bracket the next n launches of kernel `kernel` made by

@@ -11,8 +11,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["attn_fwd", "attn_bwd", "attn_decode", "rope_apply", "workspace_bytes", "decode_workspace_bytes", "AttnError",
-           "library_path", "Params"]
+__all__ = ["attn_fwd", "attn_bwd", "attn_decode", "rope_apply", "attn_fwd_f32", "attn_bwd_f32", "rope_apply_f32",
+           "workspace_bytes", "decode_workspace_bytes", "AttnError", "library_path", "Params"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libbwattn.so")
@@ -65,6 +65,12 @@ def load():
         lib.attn_fwd.argtypes = [P, V, V, V, V, V, V, V, V, ctypes.c_size_t, V]
         lib.attn_bwd.restype = ctypes.c_int
         lib.attn_bwd.argtypes = [P, V, V, V, V, V, V, V, V, V, V, V, V, ctypes.c_size_t, V]
+        lib.rope_apply_f32.restype = ctypes.c_int
+        lib.rope_apply_f32.argtypes = [P, V, V, V, ctypes.c_int32, V]
+        lib.attn_fwd_f32.restype = ctypes.c_int
+        lib.attn_fwd_f32.argtypes = [P, V, V, V, V, V, V, V, V, ctypes.c_size_t, V]
+        lib.attn_bwd_f32.restype = ctypes.c_int
+        lib.attn_bwd_f32.argtypes = [P, V, V, V, V, V, V, V, V, V, V, V, V, ctypes.c_size_t, V]
         lib.attn_decode.restype = ctypes.c_int
         lib.attn_decode.argtypes = [P, ctypes.c_int32, V, V, V, V, V, V, V, ctypes.c_size_t, V]
         lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
@@ -93,11 +99,12 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def _check_bhsd(name, t, shape=None):
+def _check_bhsd(name, t, shape=None, f32=False):
     import torch
 
-    if t.dtype != torch.bfloat16 or t.dim() != 4 or not t.is_contiguous() or not t.is_cuda:
-        raise AttnError("%s must be a contiguous bf16 CUDA tensor [B,H,S,D]" % name)
+    dt = torch.float32 if f32 else torch.bfloat16
+    if t.dtype != dt or t.dim() != 4 or not t.is_contiguous() or not t.is_cuda:
+        raise AttnError("%s must be a contiguous %s CUDA tensor [B,H,S,D]" % (name, "fp32" if f32 else "bf16"))
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise AttnError("%s has shape %r, expected %r" % (name, tuple(t.shape), tuple(shape)))
 
@@ -128,54 +135,73 @@ def _workspace(params, which, workspace, device):
     return workspace, workspace.numel() * workspace.element_size()
 
 
-def rope_apply(x, positions=None, theta=1e4, inverse=False, out=None):
-    """RoPE of x (bf16 [B,H,S,D]) at positions (int32 [B,S] or None)."""
+def _rope(fn, f32, x, positions, theta, inverse, out):
     import torch
 
-    _check_bhsd("x", x)
+    _check_bhsd("x", x, f32=f32)
     B, H, S, D = x.shape
     _check_bs("positions", positions, B, S)
     if out is None:
         out = torch.empty_like(x)
-    _check_bhsd("out", out, x.shape)
+    _check_bhsd("out", out, x.shape, f32=f32)
     p = make_params(B, H, S, D, theta=theta)
-    _raise(load().rope_apply(ctypes.byref(p), _ptr(x), _ptr(out), _ptr(positions), int(bool(inverse)), _stream()))
+    _raise(fn(ctypes.byref(p), _ptr(x), _ptr(out), _ptr(positions), int(bool(inverse)), _stream()))
     return out
 
 
-def attn_fwd(q, k, v, segment_ids=None, positions=None, theta=0.0, causal=True, scale=0.0, kv_chunk=0, out=None,
-             lse=None, workspace=None):
-    """Blockwise exact attention forward; returns (o bf16 [B,H,S,D], lse fp32 [B,H,S])."""
+def rope_apply(x, positions=None, theta=1e4, inverse=False, out=None):
+    """RoPE of x (bf16 [B,H,S,D]) at positions (int32 [B,S] or None)."""
+    return _rope(load().rope_apply, False, x, positions, theta, inverse, out)
+
+
+def rope_apply_f32(x, positions=None, theta=1e4, inverse=False, out=None):
+    """RoPE of x (fp32 [B,H,S,D]) at positions (int32 [B,S] or None)."""
+    return _rope(load().rope_apply_f32, True, x, positions, theta, inverse, out)
+
+
+def _fwd(fn, f32, q, k, v, segment_ids, positions, theta, causal, scale, kv_chunk, out, lse, workspace):
     import torch
 
-    _check_bhsd("q", q)
+    _check_bhsd("q", q, f32=f32)
     B, H, S, D = q.shape
-    _check_bhsd("k", k, q.shape)
-    _check_bhsd("v", v, q.shape)
+    _check_bhsd("k", k, q.shape, f32=f32)
+    _check_bhsd("v", v, q.shape, f32=f32)
     _check_bs("segment_ids", segment_ids, B, S)
     _check_bs("positions", positions, B, S)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
-    _check_bhsd("out", out, q.shape)
+    _check_bhsd("out", out, q.shape, f32=f32)
     p = make_params(B, H, S, D, theta=theta, causal=causal, scale=scale, kv_chunk=kv_chunk)
-    ws, nbytes = _workspace(p, 0, workspace, q.device)
-    _raise(load().attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(segment_ids), _ptr(positions), _ptr(out),
-                           _ptr(lse), _ptr(ws), nbytes, _stream()))
+    ws, nbytes = _workspace(p, 2 if f32 else 0, workspace, q.device)
+    _raise(fn(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(segment_ids), _ptr(positions), _ptr(out), _ptr(lse),
+              _ptr(ws), nbytes, _stream()))
     return out, lse
 
 
-def attn_bwd(q, k, v, o, lse, dout, segment_ids=None, positions=None, theta=0.0, causal=True, scale=0.0, kv_chunk=0,
-             dq=None, dk=None, dv=None, workspace=None):
-    """Backward of attn_fwd; returns (dq, dk, dv) bf16 [B,H,S,D] with respect to
-    the un-rotated q and k and to v."""
+def attn_fwd(q, k, v, segment_ids=None, positions=None, theta=0.0, causal=True, scale=0.0, kv_chunk=0, out=None,
+             lse=None, workspace=None):
+    """Blockwise exact attention forward; returns (o bf16 [B,H,S,D], lse fp32 [B,H,S])."""
+    return _fwd(load().attn_fwd, False, q, k, v, segment_ids, positions, theta, causal, scale, kv_chunk, out, lse,
+                workspace)
+
+
+def attn_fwd_f32(q, k, v, segment_ids=None, positions=None, theta=0.0, causal=True, scale=0.0, kv_chunk=0, out=None,
+                 lse=None, workspace=None):
+    """attn_fwd on fp32 tensors; returns (o fp32 [B,H,S,D], lse fp32 [B,H,S])."""
+    return _fwd(load().attn_fwd_f32, True, q, k, v, segment_ids, positions, theta, causal, scale, kv_chunk, out, lse,
+                workspace)
+
+
+def _bwd(fn, f32, q, k, v, o, lse, dout, segment_ids, positions, theta, causal, scale, kv_chunk, dq, dk, dv,
+         workspace):
     import torch
 
-    _check_bhsd("q", q)
+    _check_bhsd("q", q, f32=f32)
     B, H, S, D = q.shape
     for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
-        _check_bhsd(name, t, q.shape)
+        _check_bhsd(name, t, q.shape, f32=f32)
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, S) or not lse.is_contiguous():
         raise AttnError("lse must be a contiguous fp32 tensor [B,H,S]")
     _check_bs("segment_ids", segment_ids, B, S)
@@ -184,13 +210,27 @@ def attn_bwd(q, k, v, o, lse, dout, segment_ids=None, positions=None, theta=0.0,
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-        _check_bhsd(name, t, q.shape)
+        _check_bhsd(name, t, q.shape, f32=f32)
     p = make_params(B, H, S, D, theta=theta, causal=causal, scale=scale, kv_chunk=kv_chunk)
-    ws, nbytes = _workspace(p, 1, workspace, q.device)
-    _raise(load().attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
-                           _ptr(segment_ids), _ptr(positions), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), nbytes,
-                           _stream()))
+    ws, nbytes = _workspace(p, 3 if f32 else 1, workspace, q.device)
+    _raise(fn(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(segment_ids),
+              _ptr(positions), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), nbytes, _stream()))
     return dq, dk, dv
+
+
+def attn_bwd(q, k, v, o, lse, dout, segment_ids=None, positions=None, theta=0.0, causal=True, scale=0.0, kv_chunk=0,
+             dq=None, dk=None, dv=None, workspace=None):
+    """Backward of attn_fwd; returns (dq, dk, dv) bf16 [B,H,S,D] with respect to
+    the un-rotated q and k and to v."""
+    return _bwd(load().attn_bwd, False, q, k, v, o, lse, dout, segment_ids, positions, theta, causal, scale, kv_chunk,
+                dq, dk, dv, workspace)
+
+
+def attn_bwd_f32(q, k, v, o, lse, dout, segment_ids=None, positions=None, theta=0.0, causal=True, scale=0.0,
+                 kv_chunk=0, dq=None, dk=None, dv=None, workspace=None):
+    """Backward of attn_fwd_f32; returns fp32 (dq, dk, dv) [B,H,S,D]."""
+    return _bwd(load().attn_bwd_f32, True, q, k, v, o, lse, dout, segment_ids, positions, theta, causal, scale,
+                kv_chunk, dq, dk, dv, workspace)
 
 
 def decode_workspace_bytes(params: Params, n_q: int) -> int:

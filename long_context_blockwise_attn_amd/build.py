@@ -18,22 +18,28 @@ OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbwattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["prep.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "bwattn.cpp"]
+SOURCES = ["prep.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_f32.hip", "bwattn.cpp"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
     "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
     # no packed fp32 instructions (v_pk_*_f32) anywhere
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # MFMA accumulators in VGPRs; AGPRs only take spills
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
+# MFMA accumulators in VGPRs (AGPRs only take spills) for the bf16 kernels,
+# whose softmax reads the score accumulators directly.  The fp32 kernels keep
+# the compiler's default AGPR accumulators: their dQ and dK/dV kernels need
+# more than 256 registers per lane, and with the VGPR form the allocator
+# there placed an MFMA source inside the MFMA's own 16-register destination.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+AGPR_ACCUMULATORS = {"attn_f32.hip"}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, src + ".o")
     lang = [] if src.endswith(".hip") else ["-x", "hip"]
-    cmd = [HIPCC] + COMMON + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    form = [] if src in AGPR_ACCUMULATORS else VGPR_FORM
+    cmd = [HIPCC] + COMMON + form + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))

@@ -148,7 +148,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
   TileFill<BK, D / 8, NW, 2> rfill;  // K and V rows
   rfill.init(D * 2, tid);
   auto load = [&](int t, char* buf) {
-    const uint32_t rbytes = (uint32_t)(S - t * BK) * D * 2;
+    const uint32_t rbytes = (uint32_t)min(S - t * BK, BK) * D * 2;  // rows past S read zero
     rfill.fill(kh + (int64_t)t * BK * D, rbytes, buf);
     rfill.fill(vh + (int64_t)t * BK * D, rbytes, buf + KT::kBytes);
     if (use_seg && w == 0) row64_to_lds(segb, t * BK, S, buf + SEG_OFF, lane);
@@ -306,7 +306,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
   TileFill<BQT, D / 8, NW, 2> rfill;  // Q and dO rows
   rfill.init(D * 2, tid);
   auto load = [&](int t, char* buf) {
-    const uint32_t rbytes = (uint32_t)(S - t * BQT) * D * 2;
+    const uint32_t rbytes = (uint32_t)min(S - t * BQT, BQT) * D * 2;  // rows past S read zero
     rfill.fill(qh + (int64_t)t * BQT * D, rbytes, buf);
     rfill.fill(dh + (int64_t)t * BQT * D, rbytes, buf + QT::kBytes);
     if (w == 0) {

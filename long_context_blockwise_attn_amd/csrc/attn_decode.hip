@@ -56,18 +56,19 @@ __global__ __launch_bounds__(64) void attn_decode_partial_kernel(DecodeArgs a) {
   const int lim = a.causal ? S - nq + l32 : S - 1;  // last key this row sees
   const int first_limited = a.causal ? S - nq : S - 1;  // keys above this are masked for some row
 
-  const int64_t base = (int64_t)bh * S * D;
-  const __amdgpu_buffer_rsrc_t kr =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + base), (short)0, S * D * 2, 0x00020000);
-  const __amdgpu_buffer_rsrc_t vr =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(a.v + base), (short)0, S * D * 2, 0x00020000);
+  // buffers over this chunk's keys (a chunk holds at most kDecodeMaxChunk
+  // keys, so byte offsets stay far below 2^31)
+  const int64_t base = ((int64_t)bh * S + k0) * D;
+  const int nbytes = max(k1 - k0, 0) * D * 2;
+  const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + base), (short)0, nbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void*)(a.v + base), (short)0, nbytes, 0x00020000);
   auto load_k = [&](int t0, bf16x8 (&kk)[NDC]) {
-    const uint32_t off = ((uint32_t)(t0 + l32) * D + 8 * hl) * 2;
+    const uint32_t off = ((uint32_t)(t0 - k0 + l32) * D + 8 * hl) * 2;
 #pragma unroll
     for (int dc = 0; dc < NDC; ++dc) kk[dc] = buffer_b128(kr, off + 32 * dc);
   };
   auto load_v = [&](int t0, bf16x8 (&vv)[NV]) {
-    const uint32_t off = (uint32_t)t0 * D * 2 + lane * 16;
+    const uint32_t off = (uint32_t)(t0 - k0) * D * 2 + lane * 16;
 #pragma unroll
     for (int i = 0; i < NV; ++i) vv[i] = buffer_b128(vr, off + i * 1024);
   };

@@ -108,8 +108,10 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   kfill.init(D * 2, tid);
   vfill.init(a.sp * 2, tid);
   auto load = [&](int t, char* buf) {
-    kfill.fill(kh + (int64_t)t * BK * D, (uint32_t)(S - t * BK) * D * 2, buf);
-    vfill.fill(vth + t * BK, (uint32_t)(D * a.sp - t * BK) * 2, buf + KT::kBytes);
+    kfill.fill(kh + (int64_t)t * BK * D, (uint32_t)min(S - t * BK, BK) * D * 2, buf);
+    // every read stays inside the padded V^T of this head; the bound is only
+    // kept below 2^32
+    vfill.fill(vth + t * BK, (uint32_t)min(((int64_t)D * a.sp - t * BK) * 2, (int64_t)0xfffffff0), buf + KT::kBytes);
     if (use_seg && w == 0) row64_to_lds(segb, t * BK, S, buf + SEG_OFF, lane);
   };
   // vector-memory instructions this wave issues per tile

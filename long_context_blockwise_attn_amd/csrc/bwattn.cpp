@@ -88,36 +88,42 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Plan {
   int B, H, S, D, Sp;
-  bool rope, seg;
+  bool rope, f32;
+  int bq, bkv;  // own rows of the query-stationary and of the key-stationary kernel
   int nblk, n_qtiles, n_ktiles, n_bkv, n_bq;
   size_t off_qr, off_kr, off_vt, off_delta, off_blk, off_qrange, off_krange, total;
 };
 
-// Workspace layout.  The segment-dependent parts are always reserved so that
-// the size depends only on the parameters.
-Plan make_plan(const attn_params* p, int which) {
+// Workspace layout of the forward (which = 0) or backward (which = 1) of the
+// bf16 or the fp32 path.  The segment-dependent parts are always reserved so
+// that the size depends only on the parameters.
+Plan make_plan(const attn_params* p, int which, bool f32) {
   Plan pl{};
   pl.B = p->batch;
   pl.H = p->heads;
   pl.S = p->seqlen;
   pl.D = p->head_dim;
   pl.rope = p->rope_theta > 0.0;
+  pl.f32 = f32;
+  pl.bq = f32 ? (which == 0 ? kF32FwdBlockQ : kF32DqBlockQ) : kFwdBlockQ;
+  pl.bkv = f32 ? kF32BwdBlockK : kBwdBlockK;
   pl.nblk = (pl.S + kSegBlock - 1) / kSegBlock;
-  pl.n_qtiles = (pl.S + kFwdBlockQ - 1) / kFwdBlockQ;
+  pl.n_qtiles = (pl.S + pl.bq - 1) / pl.bq;
   pl.n_ktiles = (pl.S + kFwdBlockK - 1) / kFwdBlockK;
-  pl.n_bkv = (pl.S + kBwdBlockK - 1) / kBwdBlockK;
+  pl.n_bkv = (pl.S + pl.bkv - 1) / pl.bkv;
   pl.n_bq = (pl.S + kBwdBlockQ - 1) / kBwdBlockQ;
   pl.Sp = (pl.S + 63) / 64 * 64;
+  const size_t esize = f32 ? 4 : 2;
   size_t n = (size_t)pl.B * pl.H * pl.S * pl.D;
   size_t nt = (size_t)pl.B * pl.H * pl.Sp * pl.D;  // transposed copies
   size_t off = 0;
   if (pl.rope) {
     pl.off_qr = off;
-    off += align256(n * 2);
+    off += align256(n * esize);
     pl.off_kr = off;
-    off += align256(n * 2);
+    off += align256(n * esize);
   }
-  if (which == 0) {
+  if (which == 0 && !f32) {
     pl.off_vt = off;
     off += align256(nt * 2);
   }
@@ -179,14 +185,20 @@ int prepare(const attn_params* p, const Plan& pl, const void* q, const void* k, 
     r.D = pl.D;
     r.inverse = 0;
     fill_turns(r.turns, pl.D, p->rope_theta);
-    r.x = (const uint16_t*)q;
-    r.y = (uint16_t*)(ws + pl.off_qr);
-    int rc = hip_status(timed_launch(ATTN_KERNEL_ROPE, st, [&] { return launch_rope(r, st); }), "rope(q) launch");
-    if (rc) return rc;
-    r.x = (const uint16_t*)k;
-    r.y = (uint16_t*)(ws + pl.off_kr);
-    rc = hip_status(timed_launch(ATTN_KERNEL_ROPE, st, [&] { return launch_rope(r, st); }), "rope(k) launch");
-    if (rc) return rc;
+    const void* src[2] = {q, k};
+    const size_t dst[2] = {pl.off_qr, pl.off_kr};
+    const char* what[2] = {"rope(q) launch", "rope(k) launch"};
+    for (int i = 0; i < 2; ++i) {
+      int rc = hip_status(timed_launch(ATTN_KERNEL_ROPE, st,
+                                       [&] {
+                                         if (pl.f32) return launch_rope_f32(r, (const float*)src[i], (float*)(ws + dst[i]), st);
+                                         r.x = (const uint16_t*)src[i];
+                                         r.y = (uint16_t*)(ws + dst[i]);
+                                         return launch_rope(r, st);
+                                       }),
+                          what[i]);
+      if (rc) return rc;
+    }
   }
   if (seg) {
     int2* blk = (int2*)(ws + pl.off_blk);
@@ -200,7 +212,7 @@ int prepare(const attn_params* p, const Plan& pl, const void* q, const void* k, 
     t.causal = p->causal;
     // query tiles -> K/V tile ranges (forward and dQ)
     t.out = (int2*)(ws + pl.off_qrange);
-    t.own_rows = kFwdBlockQ;
+    t.own_rows = pl.bq;
     t.other_rows = kFwdBlockK;
     t.n_own = pl.n_qtiles;
     t.n_other = pl.n_ktiles;
@@ -210,7 +222,7 @@ int prepare(const attn_params* p, const Plan& pl, const void* q, const void* k, 
     if (bwd) {
       // key tiles -> query tile ranges (dK/dV)
       t.out = (int2*)(ws + pl.off_krange);
-      t.own_rows = kBwdBlockK;
+      t.own_rows = pl.bkv;
       t.other_rows = kBwdBlockQ;
       t.n_own = pl.n_bkv;
       t.n_other = pl.n_bq;
@@ -222,9 +234,34 @@ int prepare(const attn_params* p, const Plan& pl, const void* q, const void* k, 
   return ATTN_OK;
 }
 
+// Arguments shared by the fp32 kernels; the caller sets the per-kernel
+// tile counts and range table.
+F32Args f32_args(const attn_params* p, const Plan& pl, const void* q, const void* k, const void* v,
+                 const int32_t* seg, const int32_t* pos, char* ws) {
+  F32Args a{};
+  a.q = pl.rope ? (const float*)(ws + pl.off_qr) : (const float*)q;
+  a.k = pl.rope ? (const float*)(ws + pl.off_kr) : (const float*)k;
+  a.v = (const float*)v;
+  a.seg = seg;
+  a.pos = pos;
+  a.blk = seg ? (const int2*)(ws + pl.off_blk) : nullptr;
+  a.B = pl.B;
+  a.H = pl.H;
+  a.S = pl.S;
+  a.nblk = pl.nblk;
+  a.scale = scale_of(p);
+  a.scale_log2 = a.scale * 1.4426950408889634f;
+  a.causal = p->causal;
+  a.chunk_tiles = p->kv_chunk / kFwdBlockK;
+  a.rope = pl.rope ? 1 : 0;
+  if (pl.rope) fill_turns(a.turns, pl.D, p->rope_theta);
+  return a;
+}
+
 // Decode workspace: rotated query rows, then the chunk states.  About 2048
 // waves (8 per CU) keep enough K/V bytes in flight to cover HBM latency; a
-// chunk has at least 256 keys and a multiple of kDecodeTile.
+// chunk is a multiple of kDecodeTile keys, at least 256 (unless the cache is
+// shorter) and at most kDecodeMaxChunk.
 struct DecodePlan {
   int n_chunks, chunk;
   size_t off_qr, off_po, off_ml, total;
@@ -236,7 +273,7 @@ DecodePlan make_decode_plan(const attn_params* p, int n_q) {
   const int S = p->seqlen;
   int64_t want = std::max<int64_t>(1, (2048 + bh - 1) / bh);
   int64_t most = std::max(1, (S + 255) / 256);
-  int64_t n = std::min(want, most);
+  int64_t n = std::max(std::min(want, most), (int64_t)(S + kDecodeMaxChunk - 1) / kDecodeMaxChunk);
   int64_t chunk = (S + n - 1) / n;
   chunk = (chunk + kDecodeTile - 1) / kDecodeTile * kDecodeTile;
   d.chunk = (int)chunk;
@@ -278,12 +315,12 @@ const char* attn_last_error(void) { return g_err; }
 
 size_t attn_workspace_bytes(const attn_params* p, int32_t which) {
   if (check_params(p) != ATTN_OK) return 0;
-  if (which != 0 && which != 1) {
-    fail(ATTN_ERR_INVALID_ARG, "which must be 0 (forward) or 1 (backward)");
+  if (which < 0 || which > 3) {
+    fail(ATTN_ERR_INVALID_ARG, "which must be 0 (attn_fwd), 1 (attn_bwd), 2 (attn_fwd_f32) or 3 (attn_bwd_f32)");
     return 0;
   }
   g_err[0] = 0;
-  return make_plan(p, which).total;
+  return make_plan(p, which & 1, which >= 2).total;
 }
 
 int rope_apply(const attn_params* p, const void* x, void* y, const int32_t* positions, int32_t inverse,
@@ -323,7 +360,7 @@ int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, 
   const void* ptrs[] = {q, k, v, o, lse, segment_ids, positions, workspace};
   for (const void* ptr : ptrs)
     if (!aligned16(ptr)) return fail(ATTN_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
-  Plan pl = make_plan(p, 0);
+  Plan pl = make_plan(p, 0, false);
   if (workspace == nullptr || workspace_bytes < pl.total)
     return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", pl.total, workspace_bytes,
                 workspace ? "" : " (NULL)");
@@ -379,7 +416,7 @@ int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v, 
   const void* ptrs[] = {q, k, v, o, lse, d_o, segment_ids, positions, dq, dk, dv, workspace};
   for (const void* ptr : ptrs)
     if (!aligned16(ptr)) return fail(ATTN_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
-  Plan pl = make_plan(p, 1);
+  Plan pl = make_plan(p, 1, false);
   if (workspace == nullptr || workspace_bytes < pl.total)
     return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", pl.total, workspace_bytes,
                 workspace ? "" : " (NULL)");
@@ -424,6 +461,110 @@ int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v, 
   rc = hip_status(timed_launch(ATTN_KERNEL_BWD_DQ, st, [&] { return launch_attn_bwd_dq(a, pl.D, st); }), "attn_bwd dq launch");
   if (rc) return rc;
   rc = hip_status(timed_launch(ATTN_KERNEL_BWD_DKDV, st, [&] { return launch_attn_bwd_dkdv(a, pl.D, st); }), "attn_bwd dkdv launch");
+  if (rc) return rc;
+  g_err[0] = 0;
+  return ATTN_OK;
+}
+
+int rope_apply_f32(const attn_params* p, const float* x, float* y, const int32_t* positions, int32_t inverse,
+                   void* stream) {
+  int rc = check_params(p);
+  if (rc) return rc;
+  if (!(p->rope_theta > 0.0)) return fail(ATTN_ERR_INVALID_ARG, "rope_apply_f32 needs rope_theta > 0");
+  if (x == nullptr || y == nullptr) return fail(ATTN_ERR_INVALID_ARG, "x and y must not be NULL");
+  if (!aligned16(x) || !aligned16(y) || !aligned16(positions))
+    return fail(ATTN_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  if (inverse != 0 && inverse != 1) return fail(ATTN_ERR_INVALID_ARG, "inverse must be 0 or 1");
+  rc = check_device();
+  if (rc) return rc;
+  RopeArgs r{};
+  r.pos = positions;
+  r.B = p->batch;
+  r.H = p->heads;
+  r.S = p->seqlen;
+  r.D = p->head_dim;
+  r.inverse = inverse;
+  fill_turns(r.turns, p->head_dim, p->rope_theta);
+  hipStream_t st = (hipStream_t)stream;
+  rc = hip_status(timed_launch(ATTN_KERNEL_ROPE, st, [&] { return launch_rope_f32(r, x, y, st); }), "rope launch");
+  if (rc) return rc;
+  g_err[0] = 0;
+  return ATTN_OK;
+}
+
+int attn_fwd_f32(const attn_params* p, const float* q, const float* k, const float* v, const int32_t* segment_ids,
+                 const int32_t* positions, float* o, float* lse, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  int rc = check_params(p);
+  if (rc) return rc;
+  if (!q || !k || !v || !o || !lse) return fail(ATTN_ERR_INVALID_ARG, "q, k, v, o and lse must not be NULL");
+  const void* ptrs[] = {q, k, v, o, lse, segment_ids, positions, workspace};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return fail(ATTN_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  Plan pl = make_plan(p, 0, true);
+  if (workspace == nullptr || workspace_bytes < pl.total)
+    return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", pl.total, workspace_bytes,
+                workspace ? "" : " (NULL)");
+  rc = check_device();
+  if (rc) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  rc = prepare(p, pl, q, k, segment_ids, positions, ws, false, st);
+  if (rc) return rc;
+  F32Args a = f32_args(p, pl, q, k, v, segment_ids, positions, ws);
+  a.out_o = o;
+  a.out_lse = lse;
+  a.range = segment_ids ? (const int2*)(ws + pl.off_qrange) : nullptr;
+  a.n_own = pl.n_qtiles;
+  a.n_other = pl.n_ktiles;
+  rc = hip_status(timed_launch(ATTN_KERNEL_FWD_F32, st, [&] { return launch_attn_fwd_f32(a, pl.D, st); }),
+                  "attn_fwd_f32 launch");
+  if (rc) return rc;
+  g_err[0] = 0;
+  return ATTN_OK;
+}
+
+int attn_bwd_f32(const attn_params* p, const float* q, const float* k, const float* v, const float* o,
+                 const float* lse, const float* d_o, const int32_t* segment_ids, const int32_t* positions, float* dq,
+                 float* dk, float* dv, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_params(p);
+  if (rc) return rc;
+  if (!q || !k || !v || !o || !lse || !d_o || !dq || !dk || !dv)
+    return fail(ATTN_ERR_INVALID_ARG, "q, k, v, o, lse, d_o, dq, dk and dv must not be NULL");
+  const void* ptrs[] = {q, k, v, o, lse, d_o, segment_ids, positions, dq, dk, dv, workspace};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return fail(ATTN_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  Plan pl = make_plan(p, 1, true);
+  if (workspace == nullptr || workspace_bytes < pl.total)
+    return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", pl.total, workspace_bytes,
+                workspace ? "" : " (NULL)");
+  rc = check_device();
+  if (rc) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  rc = prepare(p, pl, q, k, segment_ids, positions, ws, true, st);
+  if (rc) return rc;
+  F32Args a = f32_args(p, pl, q, k, v, segment_ids, positions, ws);
+  a.o = o;
+  a.dout = d_o;
+  a.lse = lse;
+  a.ndelta = (float*)(ws + pl.off_delta);
+  a.nlse2 = (float*)(ws + pl.off_delta + align256((size_t)pl.B * pl.H * pl.S * 4));
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  // dQ first: it also forms Delta = <dO, O> per row, which dK/dV reads
+  a.range = segment_ids ? (const int2*)(ws + pl.off_qrange) : nullptr;
+  a.n_own = pl.n_qtiles;
+  a.n_other = pl.n_ktiles;
+  rc = hip_status(timed_launch(ATTN_KERNEL_BWD_DQ_F32, st, [&] { return launch_attn_bwd_dq_f32(a, pl.D, st); }),
+                  "attn_bwd_f32 dq launch");
+  if (rc) return rc;
+  a.range = segment_ids ? (const int2*)(ws + pl.off_krange) : nullptr;
+  a.n_own = pl.n_bkv;
+  a.n_other = pl.n_bq;
+  rc = hip_status(timed_launch(ATTN_KERNEL_BWD_DKDV_F32, st, [&] { return launch_attn_bwd_dkdv_f32(a, pl.D, st); }),
+                  "attn_bwd_f32 dkdv launch");
   if (rc) return rc;
   g_err[0] = 0;
   return ATTN_OK;

@@ -94,6 +94,7 @@ struct BwdArgs {
 // the chunks.
 constexpr int kDecodeTile = 32;     // keys per decode tile
 constexpr int kDecodeMaxRows = 32;  // query rows per (b,h) in one decode call
+constexpr int kDecodeMaxChunk = 1 << 20;  // keys per chunk at most
 
 struct DecodeArgs {
   const uint16_t* q;  // rotated query rows [B,H,n_q,D]
@@ -109,7 +110,47 @@ struct DecodeArgs {
   int causal;
 };
 
+// fp32 variant: the same operation on fp32 tensors with fp32 MFMAs
+// (v_mfma_f32_32x32x2_f32).  The forward keeps two waves per SIMD; the dQ and
+// dK/dV kernels hold two stationary 32-row operands plus an accumulator per
+// wave and run one wave per SIMD with the whole register file.
+constexpr int kF32FwdBlockQ = 256;  // query rows per forward workgroup (8 waves x 32 rows)
+constexpr int kF32DqBlockQ = 128;   // query rows per dQ workgroup (4 waves x 32 rows)
+constexpr int kF32BwdBlockK = 128;  // keys per dK/dV workgroup (4 waves x 32 keys)
+// streamed tiles: kFwdBlockK keys (forward, dQ) or kBwdBlockQ query rows (dK/dV)
+
+struct F32Args {
+  const float* q;      // rotated queries [B,H,S,D]
+  const float* k;      // rotated keys
+  const float* v;
+  const float* o;      // backward: forward output
+  const float* dout;   // backward: output gradient
+  const float* lse;    // backward: natural-log LSE from the forward
+  float* out_o;        // forward outputs
+  float* out_lse;
+  float* ndelta;       // [B,H,S] written by the dQ kernel: -<dO_i, O_i>
+  float* nlse2;        // [B,H,S] written by the dQ kernel: -LSE_i log2(e)
+  float* dq;
+  float* dk;
+  float* dv;
+  const int32_t* seg;  // [B,S] or null
+  const int32_t* pos;  // [B,S] or null, for the RoPE backward
+  const int2* blk;     // segment ranges per 32 rows, or null
+  const int2* range;   // per own tile of the launched kernel: [lo, hi) of streamed tiles, or null
+  int B, H, S;
+  int n_own, n_other, nblk;  // tiles of the launched kernel's own side and of the streamed side
+  float scale, scale_log2;
+  int causal;
+  int chunk_tiles;     // ring chunk in streamed tiles; 0 = natural order
+  int rope;            // apply the RoPE backward
+  double turns[64];
+};
+
 hipError_t launch_rope(const RopeArgs& a, hipStream_t st);
+hipError_t launch_rope_f32(const RopeArgs& a, const float* x, float* y, hipStream_t st);
+hipError_t launch_attn_fwd_f32(const F32Args& a, int D, hipStream_t st);
+hipError_t launch_attn_bwd_dq_f32(const F32Args& a, int D, hipStream_t st);
+hipError_t launch_attn_bwd_dkdv_f32(const F32Args& a, int D, hipStream_t st);
 hipError_t launch_transpose(const TransposeArgs& a, hipStream_t st);
 hipError_t launch_block_ranges(const int32_t* seg, int B, int S, int nblk, int2* out, hipStream_t st);
 hipError_t launch_tile_ranges(const TileRangeArgs& a, hipStream_t st);

@@ -18,17 +18,18 @@ namespace bwattn {
 
 // One thread per (b, s, group of 4 pairs); it forms the 4 angles once and
 // rotates that group in every head, so the fp64 work is shared by H rows.
-__global__ void rope_kernel(RopeArgs a) {
+// rope_group gives the thread's cosines and sines and the element offset of
+// its group in head 0 (-1: no work).
+__device__ __forceinline__ int64_t rope_group(const RopeArgs& a, float (&c)[4], float (&sn)[4]) {
   const int groups = a.D / 8;
   int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   int64_t total = (int64_t)a.B * a.S * groups;
-  if (tid >= total) return;
+  if (tid >= total) return -1;
   int g = (int)(tid % groups);
   int64_t bs = tid / groups;
   int s = (int)(bs % a.S);
   int b = (int)(bs / a.S);
   double pos = a.pos ? (double)a.pos[bs] : (double)(a.pos_base + s);
-  float c[4], sn[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     double rev = pos * a.turns[4 * g + i];  // angle in turns
@@ -38,8 +39,14 @@ __global__ void rope_kernel(RopeArgs a) {
     sn[i] = __builtin_amdgcn_sinf(f);
     if (a.inverse) sn[i] = -sn[i];
   }
+  return ((int64_t)b * a.H * a.S + s) * a.D + 8 * g;
+}
+
+__global__ void rope_kernel(RopeArgs a) {
+  float c[4], sn[4];
+  int64_t off = rope_group(a, c, sn);
+  if (off < 0) return;
   const int64_t head_stride = (int64_t)a.S * a.D;
-  int64_t off = ((int64_t)b * a.H * a.S + s) * a.D + 8 * g;
   for (int h = 0; h < a.H; ++h, off += head_stride) {
     u32x4 x = *(const u32x4*)(a.x + off);
     u32x4 y;
@@ -51,6 +58,26 @@ __global__ void rope_kernel(RopeArgs a) {
       y[i] = pack_bf16x2(y0, y1);
     }
     *(u32x4*)(a.y + off) = y;
+  }
+}
+
+// fp32 rows: the same rotation, fp32 in and out.
+__global__ void rope_f32_kernel(RopeArgs a, const float* x, float* y) {
+  float c[4], sn[4];
+  int64_t off = rope_group(a, c, sn);
+  if (off < 0) return;
+  const int64_t head_stride = (int64_t)a.S * a.D;
+  for (int h = 0; h < a.H; ++h, off += head_stride) {
+    f32x4 u = *(const f32x4*)(x + off), w = *(const f32x4*)(x + off + 4);
+    float v[8] = {u[0], u[1], u[2], u[3], w[0], w[1], w[2], w[3]};
+    float r[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      r[2 * i] = v[2 * i] * c[i] - v[2 * i + 1] * sn[i];
+      r[2 * i + 1] = v[2 * i] * sn[i] + v[2 * i + 1] * c[i];
+    }
+    *(f32x4*)(y + off) = f32x4{r[0], r[1], r[2], r[3]};
+    *(f32x4*)(y + off + 4) = f32x4{r[4], r[5], r[6], r[7]};
   }
 }
 
@@ -185,6 +212,14 @@ hipError_t launch_rope(const RopeArgs& a, hipStream_t st) {
   int threads = 256;
   int64_t blocks = (total + threads - 1) / threads;
   hipLaunchKernelGGL(rope_kernel, dim3((unsigned)blocks), dim3(threads), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_f32(const RopeArgs& a, const float* x, float* y, hipStream_t st) {
+  int64_t total = (int64_t)a.B * a.S * (a.D / 8);
+  int threads = 256;
+  int64_t blocks = (total + threads - 1) / threads;
+  hipLaunchKernelGGL(rope_f32_kernel, dim3((unsigned)blocks), dim3(threads), 0, st, a, x, y);
   return hipGetLastError();
 }
 

@@ -159,7 +159,7 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 // on LDS latency.
 template <int N, int LA, class Rd, class Mm>
 __device__ __forceinline__ void lds_mfma_pipe(Rd&& rd, Mm&& mm) {
-  bf16x8 r[N];
+  decltype(rd(0)) r[N];
 #pragma unroll
   for (int i = 0; i < LA && i < N; ++i) r[i] = rd(i);
 #pragma unroll

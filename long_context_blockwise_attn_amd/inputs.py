@@ -162,10 +162,12 @@ def make_qkv(w: Workload, device="cpu", with_grad_out: bool = False, heads: int 
     return tuple(ts)
 
 
-def random_case(B, H, S, D, seed, n_docs=0, device="cpu"):
-    """Small random case for parity tests: bf16 q, k, v, dO and, if n_docs > 0,
-    n_docs contiguous documents of random lengths (positions restart per
-    document); otherwise one document with positions 0..S-1."""
+def random_case(B, H, S, D, seed, n_docs=0, device="cpu", dtype="bf16"):
+    """Small random case for parity tests: q, k, v, dO (float32 N(0,1) from
+    numpy PCG64(seed), kept as float32 for dtype "fp32", else rounded to bf16)
+    and, if n_docs > 0, n_docs contiguous documents of random lengths
+    (positions restart per document); otherwise one document with positions
+    0..S-1."""
     import torch
 
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -176,6 +178,7 @@ def random_case(B, H, S, D, seed, n_docs=0, device="cpu"):
     else:
         seg, pos = None, np.tile(np.arange(S, dtype=np.int32), (B, 1))
     shape = (B, H, S, D)
-    ts = [torch.from_numpy(rng.standard_normal(size=shape, dtype=np.float32)).to(torch.bfloat16).to(device)
+    out_dtype = torch.float32 if dtype == "fp32" else torch.bfloat16
+    ts = [torch.from_numpy(rng.standard_normal(size=shape, dtype=np.float32)).to(out_dtype).to(device)
           for _ in range(4)]
     return ts, seg, pos

@@ -23,14 +23,14 @@ def lib():
 def declared_functions():
     text = open(os.path.join(ROOT, "include", "bwattn.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b([a-z_]+)\s*\([^;{]*\)\s*;", text)))
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\([^;{]*\)\s*;", text)))
 
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert {"attn_fwd", "attn_bwd", "rope_apply", "attn_workspace_bytes", "attn_status_string",
             "attn_last_error", "attn_profile_events", "attn_profile_count", "attn_decode",
-            "attn_decode_workspace_bytes"} <= set(names)
+            "attn_decode_workspace_bytes", "attn_fwd_f32", "attn_bwd_f32", "rope_apply_f32"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -84,6 +84,43 @@ def test_argument_errors_before_any_hip_call(lib):
     assert lib.attn_bwd(*args) == 1
 
 
+def test_f32_argument_errors_before_any_hip_call(lib):
+    import long_context_blockwise_attn_amd as bw
+
+    V = ctypes.c_void_p
+    ok = bw.make_params(1, 2, 1024, 128, theta=1e6)
+
+    def fwd(p=ok, q=16, ws=None, nbytes=0):
+        return lib.attn_fwd_f32(ctypes.byref(p), V(q) if q else None, V(32), V(48), None, None, V(64), V(80),
+                                V(ws) if ws else None, nbytes, None)
+
+    assert fwd(q=0) == 1
+    assert fwd(q=20) == 1 and b"aligned" in lib.attn_last_error()
+    assert fwd(p=bw.make_params(1, 2, 1024, 80)) == 2
+    assert fwd() == 3
+    assert fwd(ws=4096, nbytes=bw.workspace_bytes(ok, 2) - 1) == 3
+    args = [ctypes.byref(ok)] + [V(16 * (i + 1)) for i in range(12)] + [0, None]
+    args[7] = args[8] = args[12] = None
+    assert lib.attn_bwd_f32(*args) == 3
+    args[10] = None  # dk is required
+    assert lib.attn_bwd_f32(*args) == 1
+    assert lib.rope_apply_f32(ctypes.byref(bw.make_params(1, 1, 8, 64, theta=0.0)), V(16), V(16), None, 0, None) == 1
+    assert lib.rope_apply_f32(ctypes.byref(ok), V(16), V(16), None, 3, None) == 1
+
+
+def test_f32_workspace_holds_fp32_rotated_rows(lib):
+    import long_context_blockwise_attn_amd as bw
+
+    p = bw.make_params(1, 32, 32768, 128, theta=1e6)
+    n = 32 * 32768 * 128
+    f, b = bw.workspace_bytes(p, 2), bw.workspace_bytes(p, 3)
+    assert f >= 2 * n * 4 and b >= 2 * n * 4 + 2 * 32 * 32768 * 4
+    # the bf16 forward also keeps a transposed V; the fp32 one does not
+    assert bw.workspace_bytes(p, 0) == 2 * n * 2 + n * 2 + (f - 2 * n * 4)
+    p0 = bw.make_params(1, 32, 32768, 128, theta=0.0)
+    assert bw.workspace_bytes(p0, 2) == f - 2 * n * 4
+
+
 def test_workspace_size_depends_only_on_params(lib):
     import long_context_blockwise_attn_amd as bw
 
@@ -133,16 +170,17 @@ def test_decode_argument_errors_before_any_hip_call(lib):
 def test_decode_split_is_chunks_of_tiles(lib):
     """The workspace holds one partial state per chunk and row: its size pins
     the chunk count the plan chose (about 2048 chunks in all, at least 256
-    keys each)."""
+    keys and at most 2^20 keys each)."""
     import long_context_blockwise_attn_amd as bw
 
-    for B, H, S in ((1, 32, 1 << 20), (1, 2, 1000), (2, 1, 300), (1, 32, 32)):
+    for B, H, S in ((1, 32, 1 << 20), (1, 2, 1000), (2, 1, 300), (1, 32, 32), (16, 64, 1 << 22)):
         p = bw.make_params(B, H, S, 128, theta=0.0)
         n = bw.decode_workspace_bytes(p, 1)
         # no rotated-q block without RoPE: partial O (D floats) + (m, l), each 256-byte aligned
         per_chunk_o, per_chunk_ml = B * H * 128 * 4, B * H * 2 * 4
         al = lambda x: (x + 255) // 256 * 256
-        want = min(max(1, -(-2048 // (B * H))), max(1, -(-S // 256)))
+        # ... and at most 2^20 keys per chunk
+        want = max(min(max(1, -(-2048 // (B * H))), max(1, -(-S // 256))), -(-S // (1 << 20)))
         chunk = -(-(-(-S // want)) // 32) * 32
         nc = -(-S // chunk)
         assert n == al(nc * per_chunk_o) + al(nc * per_chunk_ml), (B, H, S, n, nc)
