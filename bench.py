@@ -29,10 +29,14 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "causal attention TFLOP/s fwd+bwd (32h×d128, S=32K–1M) and % of bf16 peak"
+METRIC_F32 = "causal attention TFLOP/s fwd+bwd, fp32 tensors and fp32 MFMA (32h×d128) and % of fp32 matrix peak"
 # MI355X dense bf16 MFMA peak: 256 CUs x 4 SIMDs x 1024 FLOP/clk x 2.4 GHz (the 2.5 PFLOP/s figure)
 BF16_PEAK_TFLOPS = 2516.6
+# dense fp32 MFMA peak: 256 CUs x 4 SIMDs x 64 FLOP/clk x 2.4 GHz (the 157.3 TFLOP/s figure)
+FP32_PEAK_TFLOPS = 157.3
 HBM_PEAK_GBS = 8000.0
-KERNELS = {"rope": 0, "fwd": 1, "bwd_dq": 2, "bwd_dkdv": 3, "decode": 4, "decode_merge": 5}
+KERNELS = {"rope": 0, "fwd": 1, "bwd_dq": 2, "bwd_dkdv": 3, "decode": 4, "decode_merge": 5,
+           "fwd_f32": 6, "bwd_dq_f32": 7, "bwd_dkdv_f32": 8}
 DECODE_METRIC = "decode attention HBM GB/s (1M-token KV cache, 32h×d128, one new row) and % of HBM peak"
 
 
@@ -88,7 +92,8 @@ def cpu_baseline(w, q, k, v, do, seg, pos, budget_s):
 
 # rocprofv3 kernel-name fragments of the timed kernels
 KERNEL_SYMBOLS = {"fwd": "attn_fwd_kernel", "bwd_dq": "attn_bwd_dq_kernel", "bwd_dkdv": "attn_bwd_dkdv_kernel",
-                  "decode": "attn_decode_partial_kernel"}
+                  "decode": "attn_decode_partial_kernel", "fwd_f32": "attn_fwd_f32_kernel",
+                  "bwd_dq_f32": "attn_bwd_dq_f32_kernel", "bwd_dkdv_f32": "attn_bwd_dkdv_f32_kernel"}
 
 
 def kernel_source_hash():
@@ -279,7 +284,7 @@ def decode_bench(args, w):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f32" if f32 else "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "heads": H, "head_dim": D, "cache_len": S, "n_q": nq,
                    "rope_theta": w.theta, "mask": "causal" if w.causal else "none", "parallelism": "single GPU"},
@@ -300,6 +305,8 @@ def main():
     ap.add_argument("--workload", default="llama7b_32k",
                     help="llama7b_32k (default), packing_128k, video_text_256k, full_1m, tiny, "
                          "decode_1m (attn_decode; HBM GB/s)")
+    ap.add_argument("--dtype", default="bf16", choices=["bf16", "f32"],
+                    help="bf16 (default: attn_fwd/attn_bwd) or f32 (attn_fwd_f32/attn_bwd_f32 on fp32 tensors)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=24.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -311,8 +318,9 @@ def main():
     args = ap.parse_args()
 
     if args.traffic_from:
-        write_traffic_record(args.workload, args.traffic_from[0], args.traffic_from[1],
-                             args.copy_calibration_mib or 1024, args.traffic_command)
+        # one record per workload and dtype (profiles/traffic_<workload>[_f32].json)
+        write_traffic_record(args.workload + ("_f32" if args.dtype == "f32" else ""), args.traffic_from[0],
+                             args.traffic_from[1], args.copy_calibration_mib or 1024, args.traffic_command)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -335,9 +343,10 @@ def main():
         decode_bench(args, w)
         return
     B, H, S, D = w.batch, w.heads, w.seqlen, w.head_dim
+    f32 = args.dtype == "f32"
     seg_np, pos_np, lengths = packing(w)
     w.extra["lengths"] = lengths
-    q, k, v, do = make_qkv(w, device=dev, with_grad_out=True)
+    q, k, v, do = make_qkv(w, device=dev, with_grad_out=True, dtype="fp32" if f32 else "bf16")
     seg = None if seg_np is None else torch.from_numpy(seg_np).to(dev)
     pos = torch.from_numpy(pos_np).to(dev)
     do_bwd = w.backward
@@ -346,15 +355,17 @@ def main():
     lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     pf = bw.make_params(B, H, S, D, theta=w.theta, causal=w.causal, kv_chunk=w.kv_chunk)
-    ws_f = torch.empty(bw.workspace_bytes(pf, 0), dtype=torch.uint8, device=dev)
-    ws_b = torch.empty(bw.workspace_bytes(pf, 1), dtype=torch.uint8, device=dev)
+    ws_f = torch.empty(bw.workspace_bytes(pf, 2 if f32 else 0), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(bw.workspace_bytes(pf, 3 if f32 else 1), dtype=torch.uint8, device=dev)
+    fwd_fn, bwd_fn = (bw.attn_fwd_f32, bw.attn_bwd_f32) if f32 else (bw.attn_fwd, bw.attn_bwd)
+    sfx = "_f32" if f32 else ""  # measurement-hook names of the kernels of this dtype
 
     def step():
-        bw.attn_fwd(q, k, v, seg, pos, theta=w.theta, causal=w.causal, kv_chunk=w.kv_chunk, out=o, lse=lse,
-                    workspace=ws_f)
+        fwd_fn(q, k, v, seg, pos, theta=w.theta, causal=w.causal, kv_chunk=w.kv_chunk, out=o, lse=lse,
+               workspace=ws_f)
         if do_bwd:
-            bw.attn_bwd(q, k, v, o, lse, do, seg, pos, theta=w.theta, causal=w.causal, kv_chunk=w.kv_chunk, dq=dq,
-                        dk=dk, dv=dv, workspace=ws_b)
+            bwd_fn(q, k, v, o, lse, do, seg, pos, theta=w.theta, causal=w.causal, kv_chunk=w.kv_chunk, dq=dq,
+                   dk=dk, dv=dv, workspace=ws_b)
 
     for _ in range(args.warmup):
         step()
@@ -380,7 +391,7 @@ def main():
         arr_t = (ctypes.c_void_p * n)(*[e.cuda_event for e in st])
         arr_p = (ctypes.c_void_p * n)(*[e.cuda_event for e in sp])
         keep += [arr_t, arr_p]
-        rc = lib.attn_profile_events(KERNELS[name], arr_t, arr_p, n)
+        rc = lib.attn_profile_events(KERNELS[name if name == "rope" else name + sfx], arr_t, arr_p, n)
         assert rc == 0
         ev[name] = (st, sp)
 
@@ -395,11 +406,12 @@ def main():
     ms_step = ms_total / args.steps
     kernel_ms = {}
     for name, (st, sp) in ev.items():
-        cnt = lib.attn_profile_count(KERNELS[name])
+        kid = KERNELS[name if name == "rope" else name + sfx]
+        cnt = lib.attn_profile_count(kid)
         times = [a.elapsed_time(b) for a, b in zip(st[:cnt], sp[:cnt])]
         kernel_ms[name] = {"avg_ms": float(np.mean(times)), "launches_per_step": launches[name],
                            "launches_timed": cnt}
-        lib.attn_profile_events(KERNELS[name], None, None, 0)
+        lib.attn_profile_events(kid, None, None, 0)
 
     pairs = B * visible_pairs(lengths, w.causal)
     fwd_flops = 4.0 * D * H * pairs
@@ -414,8 +426,9 @@ def main():
               key=lambda n: kernel_ms[n]["avg_ms"] * kernel_ms[n]["launches_per_step"])
     dom_flops = contractions[dom] * 2.0 * D * H * pairs
     dom_tflops = dom_flops / (kernel_ms[dom]["avg_ms"] * 1e-3) / 1e12
-    roofline = {"kernel": dom, "bound": "mfma", "achieved": dom_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": dom_tflops / BF16_PEAK_TFLOPS, "traffic": load_traffic(w.name, dom),
+    peak = FP32_PEAK_TFLOPS if f32 else BF16_PEAK_TFLOPS
+    roofline = {"kernel": dom + sfx, "bound": "mfma", "achieved": dom_tflops, "peak": peak, "unit": "TFLOP/s",
+                "frac": dom_tflops / peak, "traffic": load_traffic(w.name + sfx, dom + sfx),
                 "traffic_unit": "HBM bytes per launch", "flops_per_launch": dom_flops}
 
     if args.copy_calibration_mib > 0:
@@ -431,7 +444,7 @@ def main():
 
     mask = "causal" + ("+segment" if seg_np is not None else "")
     out = {
-        "metric": METRIC,
+        "metric": METRIC_F32 if f32 else METRIC,
         "value": tflops,
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -441,12 +454,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f32" if f32 else "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "heads": H, "head_dim": D, "seq_len": S, "rope_theta": w.theta,
                    "mask": mask, "kv_chunk": w.kv_chunk, "pass": "fwd+bwd" if do_bwd else "fwd",
                    "visible_pairs": pairs, "parallelism": "single GPU"},
-        "pct_of_bf16_peak": 100.0 * tflops / BF16_PEAK_TFLOPS,
+        ("pct_of_fp32_peak" if f32 else "pct_of_bf16_peak"): 100.0 * tflops / peak,
         "fwd_tflops": fwd_flops / (kernel_ms["fwd"]["avg_ms"] * 1e-3) / 1e12,
         "kernels_ms": {n: round(v["avg_ms"], 4) for n, v in kernel_ms.items()},
         "roofline": roofline,

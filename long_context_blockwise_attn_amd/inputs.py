@@ -144,11 +144,21 @@ def randn_bf16(shape, seed: int, device="cpu", fp32_numpy: bool = False):
     return torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
 
 
-def make_qkv(w: Workload, device="cpu", with_grad_out: bool = False, heads: int | None = None):
-    """q, k, v (and dO) bf16 [B,H,S,D] for workload w.  heads overrides H
-    (a subset of a workload's heads for cheaper tests)."""
+def make_qkv(w: Workload, device="cpu", with_grad_out: bool = False, heads: int | None = None, dtype="bf16"):
+    """q, k, v (and dO) [B,H,S,D] for workload w: bf16, or with dtype "fp32"
+    the float32 N(0,1) draws themselves (torch generator, same seeds).  heads
+    overrides H (a subset of a workload's heads for cheaper tests)."""
     H = w.heads if heads is None else heads
     shape = (w.batch, H, w.seqlen, w.head_dim)
+    if dtype == "fp32":
+        import torch
+
+        out = []
+        for i in range(4 if with_grad_out else 3):
+            g = torch.Generator(device=device)
+            g.manual_seed(w.seed * 16 + i)
+            out.append(torch.randn(shape, generator=g, device=device, dtype=torch.float32))
+        return tuple(out)
     fp32 = w.input_dtype == "fp32"
     if fp32:
         # one numpy draw for q, k, v in sequence so the seed fixes all three
