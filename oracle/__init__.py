@@ -146,3 +146,7 @@ def attn_bwd(q, k, v, dout, segment_ids=None, positions=None, theta=0.0, scale=0
                                    float(theta), float(scale), int(bool(causal)), _ptr(r), n, int(col_begin),
                                    int(col_end), _ptr(dq), _ptr(dk), _ptr(dv)))
     return dq, dk, dv
+
+
+# loss side of masked sequence packing (numpy, float64)
+from .packed_ce import packed_ce, token_ce  # noqa: E402,F401
