@@ -173,6 +173,49 @@ int attn_decode(const attn_params* p, int32_t n_q, const void* q, const void* k_
 size_t attn_decode_workspace_bytes(const attn_params* p, int32_t n_q);
 
 /* ------------------------------------------------------------------------ */
+/* Loss side of masked sequence packing.  Short examples packed into one row  */
+/* attend only to themselves (the segment mask above) and their loss is       */
+/* re-weighted so that packed training computes what training the same        */
+/* examples unpacked, one per padded row, computes (zhao9797 page "LWM (Large */
+/* World Model)", 数据 and 训练方法 with its ablation table).  The pages give  */
+/* no formula; the objective taken is the unpacked one: each example's mean   */
+/* cross-entropy over its loss tokens, averaged over the examples that have   */
+/* loss tokens:  loss = sum_t ce_t / (E n_e(t)).                               */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+  int32_t struct_size;  /* must equal sizeof(packed_ce_params)                                 */
+  int32_t batch;        /* B >= 1                                                             */
+  int32_t seqlen;       /* S >= 1; token row t = b * S + s, N = B * S <= 2^31 - 1             */
+  int32_t vocab;        /* V: a multiple of 8, 8 <= V <= 65536                                */
+  int32_t num_segments; /* example ids of a batch row lie in [0, num_segments); >= 1          */
+  float grad_scale;     /* dlogits = grad_scale * d loss / d logits                           */
+} packed_ce_params;
+
+/* Bytes of device workspace packed_ce_loss needs; 0 if the parameters are
+ * invalid. */
+size_t packed_ce_workspace_bytes(const packed_ce_params* p);
+
+/* Re-weighted cross-entropy of packed token rows and its gradient.
+ *   - logits: bf16 [N, V] (row t = b * S + s), 16-byte aligned.
+ *   - targets: int32 [N], the target token of each row; a value outside
+ *     [0, V) marks a row without loss (the last token of an example, prompt
+ *     tokens, padding).
+ *   - segment_ids: int32 [B, S] example ids (example = (b, id)); NULL means
+ *     one example per batch row.  Rows whose id lies outside
+ *     [0, num_segments) carry no loss.  Device values are not checked.
+ *   - loss: one fp32 in device memory: sum over loss rows t of
+ *     ce_t / (E n_e(t)), ce_t = logsumexp(logits[t]) - logits[t][y_t], E the
+ *     number of examples with a loss row, n_e their loss rows; 0 if E = 0.
+ *   - dlogits: bf16 [N, V] or NULL (loss only): grad_scale * (softmax(logits[t])
+ *     - onehot(y_t)) / (E n_e(t)) for loss rows, zero rows elsewhere.
+ *   - token_ce: fp32 [N] or NULL: ce_t of loss rows, 0 elsewhere.
+ * The result does not depend on the order of work (bitwise reproducible).
+ * workspace: packed_ce_workspace_bytes(p) bytes. */
+int packed_ce_loss(const packed_ce_params* p, const void* logits, const int32_t* targets,
+                   const int32_t* segment_ids, float* loss, void* dlogits, float* token_ce, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Measurement hook (for benchmarks and profilers; not needed to compute).    */
 /* ------------------------------------------------------------------------ */
 typedef enum {
@@ -185,7 +228,8 @@ typedef enum {
   ATTN_KERNEL_FWD_F32 = 6,   /* fp32 forward main kernel                              */
   ATTN_KERNEL_BWD_DQ_F32 = 7,   /* fp32 backward: dQ and Delta                        */
   ATTN_KERNEL_BWD_DKDV_F32 = 8, /* fp32 backward: dK and dV                           */
-  ATTN_KERNEL_COUNT = 9
+  ATTN_KERNEL_PACKED_CE = 9, /* packed cross-entropy: the per-row loss and gradient kernel */
+  ATTN_KERNEL_COUNT = 10
 } attn_kernel_id;
 
 /* Ask the library to bracket the next n launches of kernel `kernel` made by

@@ -12,7 +12,8 @@ import ctypes
 import os
 
 __all__ = ["attn_fwd", "attn_bwd", "attn_decode", "rope_apply", "attn_fwd_f32", "attn_bwd_f32", "rope_apply_f32",
-           "workspace_bytes", "decode_workspace_bytes", "AttnError", "library_path", "Params"]
+           "packed_ce_loss", "workspace_bytes", "decode_workspace_bytes", "packed_ce_workspace_bytes", "AttnError",
+           "library_path", "Params", "CeParams"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libbwattn.so")
@@ -38,6 +39,23 @@ class Params(ctypes.Structure):
         ("kv_chunk", ctypes.c_int32),
         ("deterministic", ctypes.c_int32),
     ]
+
+
+class CeParams(ctypes.Structure):
+    """packed_ce_params of include/bwattn.h."""
+
+    _fields_ = [
+        ("struct_size", ctypes.c_int32),
+        ("batch", ctypes.c_int32),
+        ("seqlen", ctypes.c_int32),
+        ("vocab", ctypes.c_int32),
+        ("num_segments", ctypes.c_int32),
+        ("grad_scale", ctypes.c_float),
+    ]
+
+
+def make_ce_params(B, S, V, num_segments=1, grad_scale=1.0) -> CeParams:
+    return CeParams(ctypes.sizeof(CeParams), B, S, V, int(num_segments), float(grad_scale))
 
 
 def make_params(B, H, S, D, theta=0.0, causal=True, scale=0.0, kv_chunk=0, deterministic=False) -> Params:
@@ -75,6 +93,11 @@ def load():
         lib.attn_decode.argtypes = [P, ctypes.c_int32, V, V, V, V, V, V, V, ctypes.c_size_t, V]
         lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
         lib.attn_decode_workspace_bytes.argtypes = [P, ctypes.c_int32]
+        CP = ctypes.POINTER(CeParams)
+        lib.packed_ce_workspace_bytes.restype = ctypes.c_size_t
+        lib.packed_ce_workspace_bytes.argtypes = [CP]
+        lib.packed_ce_loss.restype = ctypes.c_int
+        lib.packed_ce_loss.argtypes = [CP, V, V, V, V, V, V, V, ctypes.c_size_t, V]
         lib.attn_profile_events.restype = ctypes.c_int
         lib.attn_profile_events.argtypes = [ctypes.c_int32, V, V, ctypes.c_int32]
         lib.attn_profile_count.restype = ctypes.c_int32
@@ -268,3 +291,44 @@ def attn_decode(q, k_cache, v_cache, q_positions=None, theta=0.0, causal=True, s
     _raise(load().attn_decode(ctypes.byref(p), int(nq), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(q_positions),
                               _ptr(out), _ptr(lse), _ptr(workspace), nbytes, _stream()))
     return out, lse
+
+
+def packed_ce_workspace_bytes(params: CeParams) -> int:
+    n = load().packed_ce_workspace_bytes(ctypes.byref(params))
+    if n == 0:
+        _raise(1)
+    return int(n)
+
+
+def packed_ce_loss(logits, targets, segment_ids=None, num_segments=1, grad_scale=1.0, with_grad=True,
+                   with_token_ce=False, dlogits=None, workspace=None):
+    """Re-weighted cross-entropy of packed rows (loss side of masked sequence
+    packing): logits bf16 [B,S,V], targets int32 [B,S] (outside [0, V): no
+    loss), segment_ids int32 [B,S] example ids in [0, num_segments) or None.
+    Returns (loss fp32 [1], dlogits bf16 [B,S,V] or None, token_ce fp32 [B,S]
+    or None)."""
+    import torch
+
+    if logits.dtype != torch.bfloat16 or logits.dim() != 3 or not logits.is_contiguous() or not logits.is_cuda:
+        raise AttnError("logits must be a contiguous bf16 CUDA tensor [B,S,V]")
+    B, S, V = logits.shape
+    _check_bs("targets", targets, B, S)
+    if targets is None:
+        raise AttnError("targets are required")
+    _check_bs("segment_ids", segment_ids, B, S)
+    p = make_ce_params(B, S, V, num_segments, grad_scale)
+    need = packed_ce_workspace_bytes(p)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
+    loss = torch.empty(1, dtype=torch.float32, device=logits.device)
+    if with_grad and dlogits is None:
+        dlogits = torch.empty_like(logits)
+    if not with_grad:
+        dlogits = None
+    elif dlogits.shape != logits.shape or dlogits.dtype != torch.bfloat16 or not dlogits.is_contiguous():
+        raise AttnError("dlogits must be a contiguous bf16 tensor shaped like logits")
+    tce = torch.empty((B, S), dtype=torch.float32, device=logits.device) if with_token_ce else None
+    _raise(load().packed_ce_loss(ctypes.byref(p), _ptr(logits), _ptr(targets), _ptr(segment_ids), _ptr(loss),
+                                 _ptr(dlogits), _ptr(tce), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream()))
+    return loss, dlogits, tce

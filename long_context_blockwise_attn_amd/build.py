@@ -18,7 +18,7 @@ OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbwattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["prep.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_f32.hip", "bwattn.cpp"]
+SOURCES = ["prep.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_f32.hip", "packed_ce.hip", "bwattn.cpp"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

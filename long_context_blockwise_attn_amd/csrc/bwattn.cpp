@@ -289,6 +289,44 @@ DecodePlan make_decode_plan(const attn_params* p, int n_q) {
   return d;
 }
 
+// Packed cross-entropy: parameter checks and workspace layout.
+struct CePlan {
+  size_t off_counts, off_weights, off_wloss, total;
+};
+
+int check_ce_params(const packed_ce_params* p) {
+  if (p == nullptr) return fail(ATTN_ERR_INVALID_ARG, "params is NULL");
+  if (p->struct_size != (int32_t)sizeof(packed_ce_params))
+    return fail(ATTN_ERR_INVALID_ARG, "struct_size %d != sizeof(packed_ce_params) %d", p->struct_size,
+                (int)sizeof(packed_ce_params));
+  if (p->batch < 1 || p->seqlen < 1) return fail(ATTN_ERR_INVALID_ARG, "batch and seqlen must be >= 1");
+  if ((int64_t)p->batch * p->seqlen > ((int64_t)1 << 31) - 1)
+    return fail(ATTN_ERR_INVALID_ARG, "batch*seqlen above 2^31 - 1");
+  if (p->vocab < 8 || p->vocab % 8 != 0)
+    return fail(ATTN_ERR_INVALID_ARG, "vocab %d must be a positive multiple of 8", p->vocab);
+  if (ce_chunks_per_thread(p->vocab) < 0)
+    return fail(ATTN_ERR_UNSUPPORTED, "vocab %d above %d", p->vocab, kCeMaxVocab);
+  if (p->num_segments < 1) return fail(ATTN_ERR_INVALID_ARG, "num_segments must be >= 1");
+  if ((int64_t)p->batch * p->num_segments > ((int64_t)1 << 26))
+    return fail(ATTN_ERR_INVALID_ARG, "batch*num_segments above 2^26");
+  if (!std::isfinite(p->grad_scale)) return fail(ATTN_ERR_INVALID_ARG, "grad_scale is not finite");
+  return ATTN_OK;
+}
+
+CePlan make_ce_plan(const packed_ce_params* p) {
+  CePlan c{};
+  const size_t ne = (size_t)p->batch * p->num_segments, n = (size_t)p->batch * p->seqlen;
+  size_t off = 0;
+  c.off_counts = off;
+  off += align256(ne * 4);
+  c.off_weights = off;
+  off += align256(ne * 4);
+  c.off_wloss = off;
+  off += align256(n * 4);
+  c.total = off;
+  return c;
+}
+
 int check_decode_rows(int32_t n_q, int S) {
   if (n_q < 1 || n_q > kDecodeMaxRows)
     return fail(ATTN_ERR_INVALID_ARG, "n_q %d must be in [1, %d]", n_q, kDecodeMaxRows);
@@ -635,6 +673,58 @@ int attn_decode(const attn_params* p, int32_t n_q, const void* q, const void* k_
   rc = hip_status(
       timed_launch(ATTN_KERNEL_DECODE_MERGE, st, [&] { return launch_attn_decode_combine(a, p->head_dim, st); }),
       "attn_decode merge launch");
+  if (rc) return rc;
+  g_err[0] = 0;
+  return ATTN_OK;
+}
+
+size_t packed_ce_workspace_bytes(const packed_ce_params* p) {
+  if (check_ce_params(p) != ATTN_OK) return 0;
+  g_err[0] = 0;
+  return make_ce_plan(p).total;
+}
+
+int packed_ce_loss(const packed_ce_params* p, const void* logits, const int32_t* targets,
+                   const int32_t* segment_ids, float* loss, void* dlogits, float* token_ce, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  int rc = check_ce_params(p);
+  if (rc) return rc;
+  if (!logits || !targets || !loss) return fail(ATTN_ERR_INVALID_ARG, "logits, targets and loss must not be NULL");
+  const void* ptrs[] = {logits, dlogits, workspace};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return fail(ATTN_ERR_INVALID_ARG, "logits, dlogits and workspace must be 16-byte aligned");
+  const void* ptrs4[] = {targets, segment_ids, loss, token_ce};
+  for (const void* ptr : ptrs4)
+    if (((uintptr_t)ptr & 3u) != 0) return fail(ATTN_ERR_INVALID_ARG, "targets, segment_ids, loss and token_ce must be 4-byte aligned");
+  CePlan pl = make_ce_plan(p);
+  if (workspace == nullptr || workspace_bytes < pl.total)
+    return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", pl.total, workspace_bytes,
+                workspace ? "" : " (NULL)");
+  rc = check_device();
+  if (rc) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  CeArgs a{};
+  a.logits = (const uint16_t*)logits;
+  a.targets = targets;
+  a.seg = segment_ids;
+  a.dlogits = (uint16_t*)dlogits;
+  a.token_ce = token_ce;
+  a.loss = loss;
+  a.counts = (int*)(ws + pl.off_counts);
+  a.weights = (float*)(ws + pl.off_weights);
+  a.wloss = (float*)(ws + pl.off_wloss);
+  a.B = p->batch;
+  a.S = p->seqlen;
+  a.V = p->vocab;
+  a.num_segments = p->num_segments;
+  a.grad_scale = p->grad_scale;
+  rc = hip_status(launch_packed_ce_prologue(a, st), "packed_ce counts launch");
+  if (rc) return rc;
+  rc = hip_status(timed_launch(ATTN_KERNEL_PACKED_CE, st, [&] { return launch_packed_ce_rows(a, st); }),
+                  "packed_ce rows launch");
+  if (rc) return rc;
+  rc = hip_status(launch_packed_ce_sum(a, st), "packed_ce sum launch");
   if (rc) return rc;
   g_err[0] = 0;
   return ATTN_OK;

@@ -146,6 +146,27 @@ struct F32Args {
   double turns[64];
 };
 
+// Re-weighted cross-entropy of packed token rows (loss side of masked
+// sequence packing): token row t = b * S + s of bf16 logits [N, V].
+struct CeArgs {
+  const uint16_t* logits;  // bf16 [N, V]
+  const int32_t* targets;  // [N]; outside [0, V): row without loss
+  const int32_t* seg;      // [B, S] example ids, or null (one example per batch row)
+  uint16_t* dlogits;       // bf16 [N, V] or null
+  float* token_ce;         // [N] or null
+  float* loss;             // one float
+  int* counts;             // workspace [B * num_segments]: loss rows per example
+  float* weights;          // workspace [B * num_segments]: 1 / (E n_e)
+  float* wloss;            // workspace [N]: w_t ce_t
+  int B, S, V, num_segments;
+  float grad_scale;
+};
+constexpr int kCeMaxVocab = 65536;  // 512 threads x 16 chunks x 8 logits held in registers
+int ce_chunks_per_thread(int V);  // 16-byte chunks per thread of the row kernel, -1 if V is too large
+
+hipError_t launch_packed_ce_prologue(const CeArgs& a, hipStream_t st);
+hipError_t launch_packed_ce_rows(const CeArgs& a, hipStream_t st);
+hipError_t launch_packed_ce_sum(const CeArgs& a, hipStream_t st);
 hipError_t launch_rope(const RopeArgs& a, hipStream_t st);
 hipError_t launch_rope_f32(const RopeArgs& a, const float* x, float* y, hipStream_t st);
 hipError_t launch_attn_fwd_f32(const F32Args& a, int D, hipStream_t st);

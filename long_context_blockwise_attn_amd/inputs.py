@@ -32,6 +32,15 @@ decode_1m
     B1 H32 D128, a cache of S = 1048576 keys and values, theta 5e7, and n_q = 1
     new query row per (b,h) (token-by-token generation at 1M context); bf16
     N(0,1) q [B,H,n_q,D], k, v [B,H,S,D]; causal.
+packed_ce_32k
+    the loss side of masked sequence packing: B1 S32768 token rows of bf16
+    logits over V = 40192 (LLaMA-2's 32000 BPE tokens plus the 8192 codes of
+    the image tokenizer's VQGAN codebook), N(0, 2^2); short-context examples
+    (数据: image and video chat data packed to the context length) with
+    lengths log-uniform in [128, 8192], the last one cut; in each example of
+    length L the last round(U(0.2, 0.8) L) rows are the answer and carry a
+    uniform random target, except the example's last row (its next token
+    belongs to the next example); all other rows carry no loss (-1).
 """
 from __future__ import annotations
 
@@ -73,6 +82,8 @@ WORKLOADS = {
                                 backward=False, seed=4),
     "full_1m": Workload("full_1m", 1, 32, 128, 1048576, 5e7, kv_chunk=16384, seed=5),
     "decode_1m": Workload("decode_1m", 1, 32, 128, 1048576, 5e7, backward=False, seed=6, extra={"n_q": 1}),
+    "packed_ce_32k": Workload("packed_ce_32k", 1, 0, 0, 32768, 0.0, packing="loguniform", backward=False, seed=7,
+                              extra={"vocab": 40192, "lengths": (128, 8192)}),
 }
 
 
@@ -192,3 +203,53 @@ def random_case(B, H, S, D, seed, n_docs=0, device="cpu", dtype="bf16"):
     ts = [torch.from_numpy(rng.standard_normal(size=shape, dtype=np.float32)).to(out_dtype).to(device)
           for _ in range(4)]
     return ts, seg, pos
+
+
+def ce_targets(lengths, V, seed, batch=1):
+    """int32 [B, S] targets and segment ids for packed examples of the given
+    lengths: the last round(U(0.2, 0.8) L) rows of an example of length L are
+    its answer and get a uniform random target in [0, V), except the
+    example's last row; every other row gets -1 (no loss)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    seg, _ = segments_from_lengths(lengths, batch)
+    S = int(sum(lengths))
+    tg = np.full((batch, S), -1, dtype=np.int32)
+    for b in range(batch):
+        s0 = 0
+        for L in lengths:
+            a = max(1, int(round(rng.uniform(0.2, 0.8) * L)))
+            lo, hi = s0 + L - a, s0 + L - 1  # answer rows lo .. hi-1 (the last row has no target)
+            if hi > lo:
+                tg[b, lo:hi] = rng.integers(0, V, size=hi - lo)
+            s0 += L
+    return tg, seg
+
+
+def packed_ce_case(w: Workload, device="cpu"):
+    """(logits bf16 [B,S,V], targets int32 [B,S], segment ids int32 [B,S],
+    num_segments) of a packed cross-entropy workload."""
+    import torch
+
+    V = w.extra["vocab"]
+    lo, hi = w.extra["lengths"]
+    lengths = loguniform_lengths(w.seqlen, lo, hi, w.seed)
+    tg, seg = ce_targets(lengths, V, w.seed + 1, w.batch)
+    g = torch.Generator(device=device)
+    g.manual_seed(w.seed * 16)
+    logits = (2.0 * torch.randn((w.batch, w.seqlen, V), generator=g, device=device, dtype=torch.float32)).to(
+        torch.bfloat16)
+    return logits, torch.from_numpy(tg).to(device), torch.from_numpy(seg).to(device), len(lengths)
+
+
+def random_ce_case(B, S, V, seed, n_docs, ignore_frac=0.3):
+    """Small packed cross-entropy case (numpy PCG64): bf16 logits N(0, 2^2)
+    [B,S,V] (as float32 values), targets with a fraction of rows marked -1,
+    and n_docs contiguous examples of random lengths per row."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = (2.0 * rng.standard_normal((B, S, V))).astype(np.float32)
+    cuts = np.sort(rng.choice(np.arange(1, S), size=min(n_docs - 1, S - 1), replace=False)) if n_docs > 1 else []
+    lengths = np.diff(np.concatenate([[0], cuts, [S]])).astype(int).tolist()
+    seg, _ = segments_from_lengths(lengths, B)
+    tg = rng.integers(0, V, size=(B, S)).astype(np.int32)
+    tg[rng.random((B, S)) < ignore_frac] = -1
+    return x, tg, seg

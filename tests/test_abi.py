@@ -30,7 +30,8 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert {"attn_fwd", "attn_bwd", "rope_apply", "attn_workspace_bytes", "attn_status_string",
             "attn_last_error", "attn_profile_events", "attn_profile_count", "attn_decode",
-            "attn_decode_workspace_bytes", "attn_fwd_f32", "attn_bwd_f32", "rope_apply_f32"} <= set(names)
+            "attn_decode_workspace_bytes", "attn_fwd_f32", "attn_bwd_f32", "rope_apply_f32", "packed_ce_loss",
+            "packed_ce_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -134,7 +135,7 @@ def test_workspace_size_depends_only_on_params(lib):
 
 
 def test_profile_hook_arguments(lib):
-    assert lib.attn_profile_events(9, None, None, 0) == 1
+    assert lib.attn_profile_events(10, None, None, 0) == 1
     assert lib.attn_profile_events(1, None, None, -1) == 1
     assert lib.attn_profile_events(1, None, None, 3) == 1
     assert lib.attn_profile_events(1, None, None, 0) == 0
@@ -184,3 +185,32 @@ def test_decode_split_is_chunks_of_tiles(lib):
         chunk = -(-(-(-S // want)) // 32) * 32
         nc = -(-S // chunk)
         assert n == al(nc * per_chunk_o) + al(nc * per_chunk_ml), (B, H, S, n, nc)
+
+
+def test_packed_ce_argument_errors_before_any_hip_call(lib):
+    import long_context_blockwise_attn_amd as bw
+
+    V = ctypes.c_void_p
+    ok = bw.make_ce_params(1, 1024, 40192, num_segments=64)
+    assert ctypes.sizeof(bw.CeParams) == 24
+
+    def call(p=ok, logits=16, targets=32, seg=None, loss=48, dl=64, tce=None, ws=None, nbytes=0):
+        return lib.packed_ce_loss(ctypes.byref(p), V(logits) if logits else None, V(targets) if targets else None,
+                                  V(seg) if seg else None, V(loss) if loss else None, V(dl) if dl else None,
+                                  V(tce) if tce else None, V(ws) if ws else None, nbytes, None)
+
+    assert call(logits=0) == 1 and call(targets=0) == 1 and call(loss=0) == 1
+    assert call(logits=24) == 1 and b"aligned" in lib.attn_last_error()
+    assert call(targets=34) == 1
+    assert call(p=bw.make_ce_params(1, 1024, 40190)) == 1  # not a multiple of 8
+    assert call(p=bw.make_ce_params(1, 1024, 65544)) == 2  # above the largest vocabulary
+    assert call(p=bw.make_ce_params(1, 1024, 4096, num_segments=0)) == 1
+    assert call(p=bw.make_ce_params(1, 1024, 4096, grad_scale=float("inf"))) == 1
+    bad = bw.make_ce_params(1, 1024, 4096)
+    bad.struct_size = 20
+    assert call(p=bad) == 1
+    assert call() == 3  # no workspace
+    n = bw.packed_ce_workspace_bytes(ok)
+    assert n == 256 + 256 + 1024 * 4  # counts, weights (64 each, 256-byte aligned), one float per row
+    assert call(ws=4096, nbytes=n - 1) == 3
+    assert lib.packed_ce_workspace_bytes(ctypes.byref(bw.make_ce_params(1, 8, 7))) == 0
