@@ -36,7 +36,8 @@ BF16_PEAK_TFLOPS = 2516.6
 FP32_PEAK_TFLOPS = 157.3
 HBM_PEAK_GBS = 8000.0
 KERNELS = {"rope": 0, "fwd": 1, "bwd_dq": 2, "bwd_dkdv": 3, "decode": 4, "decode_merge": 5,
-           "fwd_f32": 6, "bwd_dq_f32": 7, "bwd_dkdv_f32": 8}
+           "fwd_f32": 6, "bwd_dq_f32": 7, "bwd_dkdv_f32": 8, "packed_ce": 9}
+CE_METRIC = "packed cross-entropy loss+gradient HBM GB/s (32768 tokens x 40192 vocab) and % of HBM peak"
 DECODE_METRIC = "decode attention HBM GB/s (1M-token KV cache, 32h×d128, one new row) and % of HBM peak"
 
 
@@ -93,7 +94,8 @@ def cpu_baseline(w, q, k, v, do, seg, pos, budget_s):
 # rocprofv3 kernel-name fragments of the timed kernels
 KERNEL_SYMBOLS = {"fwd": "attn_fwd_kernel", "bwd_dq": "attn_bwd_dq_kernel", "bwd_dkdv": "attn_bwd_dkdv_kernel",
                   "decode": "attn_decode_partial_kernel", "fwd_f32": "attn_fwd_f32_kernel",
-                  "bwd_dq_f32": "attn_bwd_dq_f32_kernel", "bwd_dkdv_f32": "attn_bwd_dkdv_f32_kernel"}
+                  "bwd_dq_f32": "attn_bwd_dq_f32_kernel", "bwd_dkdv_f32": "attn_bwd_dkdv_f32_kernel",
+                  "packed_ce": "ce_row_kernel"}
 
 
 def kernel_source_hash():
@@ -284,12 +286,114 @@ def decode_bench(args, w):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if f32 else "bf16",
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "heads": H, "head_dim": D, "cache_len": S, "n_q": nq,
                    "rope_theta": w.theta, "mask": "causal" if w.causal else "none", "parallelism": "single GPU"},
         "pct_of_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS,
         "kernels_ms": {n: round(t, 4) for n, t in kernel_ms.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    del keep
+
+
+def packed_ce_bench(args, w):
+    """One step = one packed_ce_loss call over the packed rows: loss, per-row
+    weights and the bf16 gradient of every row.  Algorithmic bytes: the
+    logits of loss rows read once, the gradient of every row written once,
+    targets and example ids read once; the path is bound by HBM."""
+    import torch
+
+    import long_context_blockwise_attn_amd as bw
+    from long_context_blockwise_attn_amd.inputs import packed_ce_case
+
+    dev = torch.device("cuda:0")
+    logits, targets, seg, ne = packed_ce_case(w, device=dev)
+    B, S, V = logits.shape
+    N = B * S
+    dl = torch.empty_like(logits)
+    ws = torch.empty(bw.packed_ce_workspace_bytes(bw.make_ce_params(B, S, V, ne)), dtype=torch.uint8, device=dev)
+    n_loss = int(((targets >= 0) & (targets < V)).sum().item())
+
+    def step():
+        bw.packed_ce_loss(logits, targets, seg, ne, dlogits=dl, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    lib = bw.load()
+    ev, keep = event_arrays(lib, torch, ["packed_ce"], {"packed_ce": args.steps})
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    st, sp = ev["packed_ce"]
+    cnt = lib.attn_profile_count(KERNELS["packed_ce"])
+    row_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(st[:cnt], sp[:cnt])]))
+    lib.attn_profile_events(KERNELS["packed_ce"], None, None, 0)
+
+    row_bytes = 2.0 * n_loss * V + 2.0 * N * V + 8.0 * N  # loss-row logits, every gradient row, targets + ids
+    step_bytes = row_bytes + 8.0 * N  # + counting pass (targets, ids)
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    row_gbs = row_bytes / (row_ms * 1e-3) / 1e9
+    roofline = {"kernel": "packed_ce", "bound": "hbm", "achieved": row_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": row_gbs / HBM_PEAK_GBS, "traffic": load_traffic(w.name, "packed_ce"),
+                "traffic_unit": "HBM bytes per launch", "bytes_per_launch": row_bytes}
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        bcopy = torch.empty_like(a)
+        bcopy.copy_(a)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        # the oracle on the first n rows (their examples as they stand), n
+        # doubled until one call takes about half the budget
+        tg = targets.cpu().numpy().reshape(-1)
+        sg = seg.cpu().numpy()
+        n, dt = 64, 0.0
+        while True:
+            x = logits[0, :n].float().cpu().numpy()
+            t_start = time.perf_counter()
+            oracle.packed_ce(x, tg[:n], sg[:, :n], ne)
+            dt = time.perf_counter() - t_start
+            if dt >= 0.5 * args.cpu_seconds or n >= S:
+                break
+            n = min(S, 2 * n)
+        nl = int(((tg[:n] >= 0) & (tg[:n] < V)).sum())
+        sample_bytes = 2.0 * nl * V + 2.0 * n * V + 8.0 * n
+        cpu = {"value": sample_bytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": "the first %d rows (%d loss rows) of the packed row, loss and full gradient, %.1f s; "
+                         "credited the same bytes per row as the GPU" % (n, nl, dt),
+               "seconds": dt}
+
+    out = {
+        "metric": CE_METRIC,
+        "value": gbs,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "seq_len": S, "vocab": V, "examples": ne, "loss_rows": n_loss,
+                   "parallelism": "single GPU"},
+        "pct_of_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS,
+        "kernels_ms": {"packed_ce": round(row_ms, 4)},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
@@ -304,7 +408,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama7b_32k",
                     help="llama7b_32k (default), packing_128k, video_text_256k, full_1m, tiny, "
-                         "decode_1m (attn_decode; HBM GB/s)")
+                         "decode_1m (attn_decode; HBM GB/s), packed_ce_32k (packed_ce_loss; HBM GB/s)")
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "f32"],
                     help="bf16 (default: attn_fwd/attn_bwd) or f32 (attn_fwd_f32/attn_bwd_f32 on fp32 tensors)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -341,6 +445,9 @@ def main():
     w = WORKLOADS[args.workload]
     if "n_q" in w.extra:
         decode_bench(args, w)
+        return
+    if "vocab" in w.extra:
+        packed_ce_bench(args, w)
         return
     B, H, S, D = w.batch, w.heads, w.seqlen, w.head_dim
     f32 = args.dtype == "f32"

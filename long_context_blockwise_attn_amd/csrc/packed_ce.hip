@@ -54,11 +54,26 @@ __global__ void ce_zero_kernel(int* p, int n) {
   if (i < n) p[i] = 0;
 }
 
+// Loss rows per example.  Packed examples are contiguous, so a wave's loss
+// rows mostly share one key: the first lane of each run of equal keys adds
+// the run's loss rows with one atomic (runs are cut by rows without loss).
 __global__ void ce_count_kernel(CeArgs a) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= (int64_t)a.B * a.S) return;
-  int key;
-  if (ce_loss_row(a, t, key)) atomicAdd(a.counts + key, 1);
+  const int lane = threadIdx.x & 63;
+  int key = -1;
+  bool lr = false;
+  if (t < (int64_t)a.B * a.S) lr = ce_loss_row(a, t, key);
+  if (!lr) key = -1;
+  const int prev = __shfl_up(key, 1, 64);
+  const bool start = lr && (lane == 0 || prev != key);
+  const uint64_t starts = __ballot(start);
+  const uint64_t loss = __ballot(lr);
+  if (start) {
+    const uint64_t later = lane == 63 ? 0ull : starts & (~0ull << (lane + 1));
+    const int end = later ? __ffsll((long long)later) - 1 : 64;  // next run start (exclusive end)
+    const uint64_t upto = end == 64 ? ~0ull : ((1ull << end) - 1);
+    atomicAdd(a.counts + key, __popcll(loss & upto & (~0ull << lane)));
+  }
 }
 
 // E = number of examples with a loss row; w_e = 1 / (E n_e) (0 if n_e = 0).
