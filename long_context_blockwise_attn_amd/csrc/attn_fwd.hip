@@ -8,21 +8,18 @@
 // the packing mask (each packed example attends only to itself, 训练方法).
 //
 // Work decomposition: a workgroup of NW waves owns 256 query rows of one
-// (batch, head); each wave owns 32 rows.  Tiles of 64 keys of K and of the
-// transposed V sit in an NSTAGE-deep LDS ring filled by buffer-to-LDS loads.
-// Scores are computed transposed, S^T = K Q^T, so each lane holds one query
-// row: the row max needs one exchange between lanes l and l^32, and the
-// running rescale of O is a per-lane scalar.  O^T = V^T P^T takes P^T straight
-// from the score registers; the transposed V copy stores each 16 keys in the
-// order those registers hold them, so both MFMA operands are plain 16-byte LDS
-// reads.
+// (batch, head); each wave owns 32 rows.  Tiles of 64 keys of K and V rows sit
+// in an NSTAGE-deep LDS ring filled by buffer-to-LDS loads.  Scores are
+// computed transposed, S^T = K Q^T, so each lane holds one query row: the row
+// max needs one exchange between lanes l and l^32, and the running rescale of
+// O is a per-lane scalar.  O^T = V^T P^T takes P^T straight from the score
+// registers; its V^T operand is read from the V rows with transposing LDS
+// reads (PTile::read_tr), which deliver the keys in the order the score
+// registers hold them, so no transposed copy of V is made.
 //
-// Software pipeline inside each wave, per K/V tile t:
-//   region 1: S^T of tile t+1 (MFMA)  interleaved with  softmax of tile t (VALU)
-//   mask of tile t+1 (only partial tiles)
-//   region 2: O^T += V^T P^T of tile t (MFMA)  interleaved with  row max of t+1
-//   lazy rescale of O for tile t+1 (rare)
-// so the matrix cores and the vector ALUs of a SIMD work at the same time.
+// Two wave groups run one phase apart (ping-pong, below): on every SIMD one
+// wave issues the matrix phase (S^T of the next tile, O^T += V^T P^T) while
+// the other runs the vector phase (mask, max, lazy rescale, softmax).
 #include "common.hpp"
 #include "kernels.hpp"
 #include "tile.hpp"
@@ -39,8 +36,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   constexpr int NDG = D / 32;  // 32-row groups of O^T over D
   constexpr float kLazy = 8.f;
   using KT = PTile<BK, D / 8>;  // K rows
-  using VT = PTile<D, BK / 8>;  // V^T rows (d), 64 keys each
-  constexpr int SEG_OFF = KT::kBytes + VT::kBytes;  // segment ids of the tile's keys
+  using VR = PTile<BK, D / 8, 2>;  // V rows (V^T read transposed)
+  constexpr int SEG_OFF = KT::kBytes + VR::kBytes;  // segment ids of the tile's keys
   constexpr int BUF = SEG_OFF + 256;
   __shared__ __attribute__((aligned(16))) char smem[NSTAGE * BUF];
 
@@ -102,16 +99,15 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   const float sl2 = a.scale_log2;
 
   const uint16_t* kh = a.k + base;
-  const uint16_t* vth = a.vt + (int64_t)bh * D * a.sp;
-  TileFill<BK, D / 8, NW> kfill;  // K rows
-  TileFill<D, BK / 8, NW> vfill;  // V^T rows
+  const uint16_t* vh = a.v + base;
+  TileFill<BK, D / 8, NW> kfill;     // K rows
+  TileFill<BK, D / 8, NW, 2> vfill;  // V rows
   kfill.init(D * 2, tid);
-  vfill.init(a.sp * 2, tid);
+  vfill.init(D * 2, tid);
   auto load = [&](int t, char* buf) {
-    kfill.fill(kh + (int64_t)t * BK * D, (uint32_t)min(S - t * BK, BK) * D * 2, buf);
-    // every read stays inside the padded V^T of this head; the bound is only
-    // kept below 2^32
-    vfill.fill(vth + t * BK, (uint32_t)min(((int64_t)D * a.sp - t * BK) * 2, (int64_t)0xfffffff0), buf + KT::kBytes);
+    const uint32_t rbytes = (uint32_t)min(S - t * BK, BK) * D * 2;  // rows past S read zero
+    kfill.fill(kh + (int64_t)t * BK * D, rbytes, buf);
+    vfill.fill(vh + (int64_t)t * BK * D, rbytes, buf + KT::kBytes);
     if (use_seg && w == 0) row64_to_lds(segb, t * BK, S, buf + SEG_OFF, lane);
   };
   // vector-memory instructions this wave issues per tile
@@ -194,8 +190,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
     lsum = rs;
   };
   auto pv = [&](const char* buf, const bf16x8 (&pk)[4]) {
-    const char* vt = buf + KT::kBytes;
-    lds_mfma_pipe<4 * NDG, 3>([&](int i) { return VT::read(vt, 32 * (i % NDG), i / NDG, lane); },
+    // V^T operand for keys 16 kc .. 16 kc + 15 (the keys of pk[kc]) and d 32 dg ..
+    const char* vr = buf + KT::kBytes;
+    lds_mfma_pipe<4 * NDG, 3>([&](int i) { return VR::read_tr(vr, 16 * (i / NDG), 32 * (i % NDG), lane); },
                               [&](int i, bf16x8 x) { o[i % NDG] = mfma32(x, pk[i / NDG], o[i % NDG]); });
   };
 

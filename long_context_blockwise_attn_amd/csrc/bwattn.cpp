@@ -87,11 +87,11 @@ int check_params(const attn_params* p) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Plan {
-  int B, H, S, D, Sp;
+  int B, H, S, D;
   bool rope, f32;
   int bq, bkv;  // own rows of the query-stationary and of the key-stationary kernel
   int nblk, n_qtiles, n_ktiles, n_bkv, n_bq;
-  size_t off_qr, off_kr, off_vt, off_delta, off_blk, off_qrange, off_krange, total;
+  size_t off_qr, off_kr, off_delta, off_blk, off_qrange, off_krange, total;
 };
 
 // Workspace layout of the forward (which = 0) or backward (which = 1) of the
@@ -112,20 +112,14 @@ Plan make_plan(const attn_params* p, int which, bool f32) {
   pl.n_ktiles = (pl.S + kFwdBlockK - 1) / kFwdBlockK;
   pl.n_bkv = (pl.S + pl.bkv - 1) / pl.bkv;
   pl.n_bq = (pl.S + kBwdBlockQ - 1) / kBwdBlockQ;
-  pl.Sp = (pl.S + 63) / 64 * 64;
   const size_t esize = f32 ? 4 : 2;
   size_t n = (size_t)pl.B * pl.H * pl.S * pl.D;
-  size_t nt = (size_t)pl.B * pl.H * pl.Sp * pl.D;  // transposed copies
   size_t off = 0;
   if (pl.rope) {
     pl.off_qr = off;
     off += align256(n * esize);
     pl.off_kr = off;
     off += align256(n * esize);
-  }
-  if (which == 0 && !f32) {
-    pl.off_vt = off;
-    off += align256(nt * 2);
   }
   if (which == 1) {
     pl.off_delta = off;  // -Delta, then -LSE log2(e)
@@ -408,22 +402,10 @@ int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, 
   char* ws = (char*)workspace;
   rc = prepare(p, pl, q, k, segment_ids, positions, ws, false, st);
   if (rc) return rc;
-  TransposeArgs ta{};
-  ta.x = (const uint16_t*)v;
-  ta.y = (uint16_t*)(ws + pl.off_vt);
-  ta.B = pl.B;
-  ta.H = pl.H;
-  ta.S = pl.S;
-  ta.D = pl.D;
-  ta.Sp = pl.Sp;
-  rc = hip_status(launch_transpose(ta, st), "transpose(v) launch");
-  if (rc) return rc;
   FwdArgs a{};
   a.q = pl.rope ? (const uint16_t*)(ws + pl.off_qr) : (const uint16_t*)q;
   a.k = pl.rope ? (const uint16_t*)(ws + pl.off_kr) : (const uint16_t*)k;
   a.v = (const uint16_t*)v;
-  a.vt = (const uint16_t*)(ws + pl.off_vt);
-  a.sp = pl.Sp;
   a.o = (uint16_t*)o;
   a.lse = lse;
   a.seg = segment_ids;

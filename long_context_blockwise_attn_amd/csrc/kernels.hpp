@@ -22,17 +22,6 @@ struct RopeArgs {
   double turns[64];  // theta^(-2i/D) / (2 pi), i < D/2
 };
 
-// Transposed copy for MFMA operands with k along the sequence: x [B,H,S,D]
-// -> y [B,H,D,Sp] (Sp = S rounded up to 64, padding zero).  Inside each group
-// of 16 positions the order is 0-3, 8-11, 4-7, 12-15 (bits 2 and 3 of the
-// position swapped), which is the order in which a 32x32x16 MFMA result
-// register block hands its k values to the next MFMA.
-struct TransposeArgs {
-  const uint16_t* x;
-  uint16_t* y;
-  int B, H, S, D, Sp;
-};
-
 struct TileRangeArgs {
   const int2* blk;  // [B, nblk] segment ranges or null (no packing mask)
   int2* out;        // [B, n_own] -> [lo, hi) over the other side's tiles
@@ -47,8 +36,6 @@ struct FwdArgs {
   const uint16_t* q;  // rotated queries [B,H,S,D]
   const uint16_t* k;  // rotated keys
   const uint16_t* v;
-  const uint16_t* vt;  // V transposed [B,H,D,Sp] (permuted within 16)
-  int sp;              // row stride of vt
   uint16_t* o;
   float* lse;          // natural log, [B,H,S]
   const int32_t* seg;  // [B,S] or null
@@ -172,7 +159,6 @@ hipError_t launch_rope_f32(const RopeArgs& a, const float* x, float* y, hipStrea
 hipError_t launch_attn_fwd_f32(const F32Args& a, int D, hipStream_t st);
 hipError_t launch_attn_bwd_dq_f32(const F32Args& a, int D, hipStream_t st);
 hipError_t launch_attn_bwd_dkdv_f32(const F32Args& a, int D, hipStream_t st);
-hipError_t launch_transpose(const TransposeArgs& a, hipStream_t st);
 hipError_t launch_block_ranges(const int32_t* seg, int B, int S, int nblk, int2* out, hipStream_t st);
 hipError_t launch_tile_ranges(const TileRangeArgs& a, hipStream_t st);
 hipError_t launch_attn_fwd(const FwdArgs& a, int D, hipStream_t st);

@@ -81,47 +81,6 @@ __global__ void rope_f32_kernel(RopeArgs a, const float* x, float* y) {
   }
 }
 
-// Transposed copy: one workgroup per (b,h) and 64 positions.  The 64 x D
-// block goes through LDS (row-padded against bank conflicts); each thread then
-// writes 16-byte runs of 8 positions of one output row d.
-__device__ __forceinline__ int perm16(int s) {
-  return (s & ~12) | ((s & 4) << 1) | ((s & 8) >> 1);  // swap bits 2 and 3
-}
-
-__global__ __launch_bounds__(256) void transpose_kernel(TransposeArgs a) {
-  __shared__ uint16_t t[64][128 + 2];
-  const int D = a.D;
-  const int nblk = a.Sp / 64;
-  const int blk = blockIdx.x % nblk;
-  const int bh = blockIdx.x / nblk;
-  const int s0 = blk * 64;
-  const uint16_t* src = a.x + (int64_t)bh * a.S * D;
-  const int cpr = D / 8;  // 16-byte chunks per input row
-  for (int c = threadIdx.x; c < 64 * cpr; c += 256) {
-    int r = c / cpr, ch = c % cpr;
-    int s = s0 + r;
-    u32x4 v = s < a.S ? *(const u32x4*)(src + (int64_t)s * D + ch * 8) : u32x4{0, 0, 0, 0};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      t[r][ch * 8 + 2 * e] = (uint16_t)(v[e] & 0xffff);
-      t[r][ch * 8 + 2 * e + 1] = (uint16_t)(v[e] >> 16);
-    }
-  }
-  __syncthreads();
-  uint16_t* dst = a.y + (int64_t)bh * D * a.Sp + s0;
-  // output row d, positions p .. p+7 of this block (8 chunks per row)
-  for (int c = threadIdx.x; c < D * 8; c += 256) {
-    int d = c / 8, p0 = (c % 8) * 8;
-    uint32_t w[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      int sa = perm16(p0 + 2 * e), sb = perm16(p0 + 2 * e + 1);  // perm16 is its own inverse
-      w[e] = (uint32_t)t[sa][d] | ((uint32_t)t[sb][d] << 16);
-    }
-    *(u32x4*)(dst + (int64_t)d * a.Sp + p0) = u32x4{w[0], w[1], w[2], w[3]};
-  }
-}
-
 // Min and max segment id of every 32-row block of every batch row.
 __global__ void block_range_kernel(const int32_t* seg, int B, int S, int nblk, int2* out) {
   int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -220,12 +179,6 @@ hipError_t launch_rope_f32(const RopeArgs& a, const float* x, float* y, hipStrea
   int threads = 256;
   int64_t blocks = (total + threads - 1) / threads;
   hipLaunchKernelGGL(rope_f32_kernel, dim3((unsigned)blocks), dim3(threads), 0, st, a, x, y);
-  return hipGetLastError();
-}
-
-hipError_t launch_transpose(const TransposeArgs& a, hipStream_t st) {
-  int64_t blocks = (int64_t)a.B * a.H * (a.Sp / 64);
-  hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
