@@ -12,7 +12,9 @@ samples it computes one by one:
     of a packed row), so those columns are complete sums, not partial ones.
 For the 1M workload the GPU runs 8 of the 32 heads: heads are independent and
 each takes the same kernel path, while the sequence length, the chunking and
-the ring order are the workload's.
+the ring order are the workload's.  The fp32 path (attn_fwd_f32 /
+attn_bwd_f32 on fp32 draws of the same workloads) runs the 32K and the 128K
+packed workloads whole, held to the fp32 bars.
 """
 import numpy as np
 import pytest
@@ -21,13 +23,18 @@ from helpers import assert_parity
 
 pytestmark = pytest.mark.gpu
 
-# workload, heads run on the GPU (None: all of the workload's), heads checked
+# workload, heads run on the GPU (None: all of the workload's), heads checked,
+# path (bf16, or fp32 tensors through attn_fwd_f32 / attn_bwd_f32 with the
+# fp32 bars of test_gpu_f32.py)
 FULL = [
-    ("llama7b_32k", None, (0, 31)),
-    ("packing_128k", None, (7,)),
-    ("video_text_256k", None, (12,)),
-    ("full_1m", 8, (3,)),
+    ("llama7b_32k", None, (0, 31), "bf16"),
+    ("packing_128k", None, (7,), "bf16"),
+    ("video_text_256k", None, (12,), "bf16"),
+    ("full_1m", 8, (3,), "bf16"),
+    ("llama7b_32k", None, (5,), "f32"),
+    ("packing_128k", None, (20,), "f32"),
 ]
+F32_BARS = dict(max_abs=2e-4, mean_abs=2e-5)
 
 
 @pytest.fixture(scope="module")
@@ -80,8 +87,10 @@ def head64(t, h):
     return t[:, h:h + 1].float().cpu().numpy().astype(np.float64)
 
 
-@pytest.mark.parametrize("name,gpu_heads,check_heads", FULL)
-def test_full_size_sampled_parity(oracle, torch_cuda, name, gpu_heads, check_heads):
+@pytest.mark.parametrize("name,gpu_heads,check_heads,path", FULL)
+def test_full_size_sampled_parity(oracle, torch_cuda, name, gpu_heads, check_heads, path):
+    import functools
+
     import long_context_blockwise_attn_amd as bw
     from long_context_blockwise_attn_amd.inputs import WORKLOADS, make_qkv, packing
 
@@ -89,16 +98,20 @@ def test_full_size_sampled_parity(oracle, torch_cuda, name, gpu_heads, check_hea
     w = WORKLOADS[name]
     H = w.heads if gpu_heads is None else gpu_heads
     S = w.seqlen
+    f32 = path == "f32"
+    bars = F32_BARS if f32 else {}
+    assert_parity_ = functools.partial(assert_parity, **bars)
+    fwd, bwd = (bw.attn_fwd_f32, bw.attn_bwd_f32) if f32 else (bw.attn_fwd, bw.attn_bwd)
     seg, pos, lengths = packing(w)
-    q, k, v, do = make_qkv(w, device="cuda", with_grad_out=True, heads=gpu_heads)
+    q, k, v, do = make_qkv(w, device="cuda", with_grad_out=True, heads=gpu_heads, dtype="fp32" if f32 else "bf16")
     dseg = None if seg is None else torch.from_numpy(seg).cuda()
     dpos = torch.from_numpy(pos).cuda()
-    print("workload %s: B%d H%d S%d D%d theta %g chunk %d docs %d backward %d" % (
-        name, w.batch, H, S, w.head_dim, w.theta, w.kv_chunk, len(lengths), w.backward), flush=True)
-    o, lse = bw.attn_fwd(q, k, v, dseg, dpos, theta=w.theta, causal=w.causal, kv_chunk=w.kv_chunk)
+    print("workload %s (%s): B%d H%d S%d D%d theta %g chunk %d docs %d backward %d" % (
+        name, path, w.batch, H, S, w.head_dim, w.theta, w.kv_chunk, len(lengths), w.backward), flush=True)
+    o, lse = fwd(q, k, v, dseg, dpos, theta=w.theta, causal=w.causal, kv_chunk=w.kv_chunk)
     grads = None
     if w.backward:
-        grads = bw.attn_bwd(q, k, v, o, lse, do, dseg, dpos, theta=w.theta, causal=w.causal, kv_chunk=w.kv_chunk)
+        grads = bwd(q, k, v, o, lse, do, dseg, dpos, theta=w.theta, causal=w.causal, kv_chunk=w.kv_chunk)
     torch.cuda.synchronize()
     print("  GPU done", flush=True)
 
@@ -108,8 +121,8 @@ def test_full_size_sampled_parity(oracle, torch_cuda, name, gpu_heads, check_hea
     for h in check_heads:
         qh, kh, vh = head64(q, h), head64(k, h), head64(v, h)
         ro, rlse = oracle.attn_fwd(qh, kh, vh, seg, pos, theta=w.theta, causal=w.causal, rows=rows)
-        eo = assert_parity(o[:, h:h + 1, rows].float().cpu().numpy(), ro, "%s h%d O" % (name, h))
-        el = assert_parity(lse[:, h:h + 1, rows].cpu().numpy(), rlse, "%s h%d LSE" % (name, h))
+        eo = assert_parity_(o[:, h:h + 1, rows].float().cpu().numpy(), ro, "%s h%d O" % (name, h))
+        el = assert_parity_(lse[:, h:h + 1, rows].cpu().numpy(), rlse, "%s h%d LSE" % (name, h))
         print("  head %d: O, LSE on %d rows, (max, mean) abs errors %s %s" % (h, len(rows), eo, el), flush=True)
         if grads is None:
             continue
@@ -117,15 +130,15 @@ def test_full_size_sampled_parity(oracle, torch_cuda, name, gpu_heads, check_hea
         doh = head64(do, h)
         rdq, _, _ = oracle.attn_bwd(qh, kh, vh, doh, seg, pos, theta=w.theta, causal=w.causal, rows=rows,
                                     col_begin=0, col_end=0)
-        eq = assert_parity(dq[:, h:h + 1, rows].float().cpu().numpy(), rdq, "%s h%d dq" % (name, h))
+        eq = assert_parity_(dq[:, h:h + 1, rows].float().cpu().numpy(), rdq, "%s h%d dq" % (name, h))
         print("  head %d: dq on %d rows, (max, mean) abs error %s" % (h, len(rows), eq), flush=True)
         for c0, c1 in wins:
             wrows = np.arange(c0, c1, dtype=np.int64)
             rdq, rdk, rdv = oracle.attn_bwd(qh, kh, vh, doh, seg, pos, theta=w.theta, causal=w.causal, rows=wrows,
                                             col_begin=c0, col_end=c1)
-            assert_parity(dq[:, h:h + 1, c0:c1].float().cpu().numpy(), rdq, "%s h%d dq [%d,%d)" % (name, h, c0, c1))
-            ek = assert_parity(dk[:, h:h + 1, c0:c1].float().cpu().numpy(), rdk, "%s h%d dk [%d,%d)" % (name, h, c0, c1))
-            ev = assert_parity(dv[:, h:h + 1, c0:c1].float().cpu().numpy(), rdv, "%s h%d dv [%d,%d)" % (name, h, c0, c1))
+            assert_parity_(dq[:, h:h + 1, c0:c1].float().cpu().numpy(), rdq, "%s h%d dq [%d,%d)" % (name, h, c0, c1))
+            ek = assert_parity_(dk[:, h:h + 1, c0:c1].float().cpu().numpy(), rdk, "%s h%d dk [%d,%d)" % (name, h, c0, c1))
+            ev = assert_parity_(dv[:, h:h + 1, c0:c1].float().cpu().numpy(), rdv, "%s h%d dv [%d,%d)" % (name, h, c0, c1))
             print("  head %d: keys [%d, %d): dk %s dv %s" % (h, c0, c1, ek, ev), flush=True)
     del q, k, v, do, o, lse, grads
     torch.cuda.empty_cache()
