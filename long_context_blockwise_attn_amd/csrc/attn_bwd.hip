@@ -121,19 +121,17 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
 
   TileWalk walk;
   if (a.qrange) {
-    int2 r = a.qrange[(int64_t)b * a.n_qtiles + qt];
-    walk.lo = r.x;
-    walk.hi = r.y;
+    walk_range(walk, a.qrange[(int64_t)b * a.n_qtiles + qt], blkb);
   } else {
     walk.lo = 0;
     walk.hi = a.causal ? min(a.n_ktiles, (min(S, Q0 + BQ) - 1) / BK + 1) : a.n_ktiles;
+    walk.blk = nullptr;
   }
   walk.ct = a.chunk_tiles;
   walk.nc = a.chunk_tiles ? (a.n_ktiles + a.chunk_tiles - 1) / a.chunk_tiles : 1;
   walk.r = a.chunk_tiles ? (Q0 / BK) / a.chunk_tiles : 0;
   walk.dir = -1;
   walk.desc = false;
-  walk.blk = blkb;
   walk.nblk = a.nblk;
   walk.rows = BK;
   walk.own = use_seg ? seg_range(blkb, a.nblk, Q0, min(BQ, S - Q0)) : make_int2(0, 0);
@@ -272,12 +270,11 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
 
   TileWalk walk;
   if (a.krange) {
-    int2 r = a.krange[(int64_t)b * a.n_bkv + kt_idx];
-    walk.lo = r.x;
-    walk.hi = r.y;
+    walk_range(walk, a.krange[(int64_t)b * a.n_bkv + kt_idx], blkb);
   } else {
     walk.lo = a.causal ? K0 / BQT : 0;
     walk.hi = a.n_bq;
+    walk.blk = nullptr;
   }
   walk.ct = a.chunk_tiles;  // a chunk of kv_chunk rows is kv_chunk / 64 tiles on both sides
   walk.nc = a.chunk_tiles ? (a.n_bq + a.chunk_tiles - 1) / a.chunk_tiles : 1;
@@ -286,7 +283,6 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
   // natural order: from the last query tile down, so that workgroups of one
   // head stream the same Q/dO tiles at the same time (L2 reuse)
   walk.desc = true;
-  walk.blk = blkb;
   walk.nblk = a.nblk;
   walk.rows = BQT;
   walk.own = use_seg ? seg_range(blkb, a.nblk, K0, min(BKV, S - K0)) : make_int2(0, 0);

@@ -126,19 +126,17 @@ __device__ __forceinline__ TileWalk query_block_walk(const F32Args& a, int b, in
   TileWalk walk;
   const int S = a.S;
   if (a.range) {
-    int2 r = a.range[(int64_t)b * a.n_own + qt];
-    walk.lo = r.x;
-    walk.hi = r.y;
+    walk_range(walk, a.range[(int64_t)b * a.n_own + qt], blkb);
   } else {
     walk.lo = 0;
     walk.hi = a.causal ? min(a.n_other, (min(S, Q0 + BQ) - 1) / BK + 1) : a.n_other;
+    walk.blk = nullptr;
   }
   walk.ct = a.chunk_tiles;
   walk.nc = a.chunk_tiles ? (a.n_other + a.chunk_tiles - 1) / a.chunk_tiles : 1;
   walk.r = a.chunk_tiles ? (Q0 / BK) / a.chunk_tiles : 0;
   walk.dir = -1;
   walk.desc = 0;
-  walk.blk = blkb;
   walk.nblk = a.nblk;
   walk.rows = BK;
   walk.own = use_seg ? seg_range(blkb, a.nblk, Q0, min(BQ, S - Q0)) : make_int2(0, 0);
@@ -463,19 +461,17 @@ void attn_bwd_dkdv_f32_kernel(F32Args a) {
 
   TileWalk walk;
   if (a.range) {
-    int2 r = a.range[(int64_t)b * a.n_own + kt_idx];
-    walk.lo = r.x;
-    walk.hi = r.y;
+    walk_range(walk, a.range[(int64_t)b * a.n_own + kt_idx], blkb);
   } else {
     walk.lo = a.causal ? K0 / BQT : 0;
     walk.hi = a.n_other;
+    walk.blk = nullptr;
   }
   walk.ct = a.chunk_tiles;
   walk.nc = a.chunk_tiles ? (a.n_other + a.chunk_tiles - 1) / a.chunk_tiles : 1;
   walk.r = a.chunk_tiles ? (K0 / BQT) / a.chunk_tiles : 0;
   walk.dir = +1;
   walk.desc = 1;  // natural order from the last query tile down (L2 reuse across workgroups)
-  walk.blk = blkb;
   walk.nblk = a.nblk;
   walk.rows = BQT;
   walk.own = use_seg ? seg_range(blkb, a.nblk, K0, min(BKV, S - K0)) : make_int2(0, 0);

@@ -74,19 +74,17 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   // K/V tile range and walk
   TileWalk walk;
   if (a.qrange) {
-    int2 r = a.qrange[(int64_t)b * a.n_qtiles + qt];
-    walk.lo = r.x;
-    walk.hi = r.y;
+    walk_range(walk, a.qrange[(int64_t)b * a.n_qtiles + qt], blkb);
   } else {
     walk.lo = 0;
     walk.hi = a.causal ? min(a.n_ktiles, (min(S, Q0 + BQ) - 1) / BK + 1) : a.n_ktiles;
+    walk.blk = nullptr;
   }
   walk.ct = a.chunk_tiles;
   walk.nc = a.chunk_tiles ? (a.n_ktiles + a.chunk_tiles - 1) / a.chunk_tiles : 1;
   walk.r = a.chunk_tiles ? (Q0 / BK) / a.chunk_tiles : 0;
   walk.dir = -1;
   walk.desc = false;
-  walk.blk = blkb;
   walk.nblk = a.nblk;
   walk.rows = BK;
   walk.own = use_seg ? seg_range(blkb, a.nblk, Q0, min(BQ, S - Q0)) : make_int2(0, 0);

@@ -22,9 +22,15 @@ struct RopeArgs {
   double turns[64];  // theta^(-2i/D) / (2 pi), i < D/2
 };
 
+// Range tables: per own tile, [lo, hi) over the other side's tiles.  Bit 30
+// of lo is set when some tile inside the range cannot hold a visible pair
+// (segment ids that are not contiguous), so a walk over it must test each
+// tile; for contiguous segments every tile in [lo, hi) is useful.
+constexpr int kRangeSparse = 1 << 30;
+
 struct TileRangeArgs {
   const int2* blk;  // [B, nblk] segment ranges or null (no packing mask)
-  int2* out;        // [B, n_own] -> [lo, hi) over the other side's tiles
+  int2* out;        // [B, n_own] -> [lo | sparse flag, hi) over the other side's tiles
   int B, S, nblk;
   int own_rows, other_rows, n_own, n_other;
   int causal, own_is_query;

@@ -160,7 +160,25 @@ __global__ void tile_range_kernel(TileRangeArgs a) {
       }
     }
   }
-  if (lane == 0) a.out[wid] = make_int2(lo, hi);
+  // does every tile in [lo, hi) meet the own tile's segment range?
+  bool sparse = false;
+  if (a.blk != nullptr && lo < hi) {
+    const int2* br = a.blk + (int64_t)b * a.nblk;
+    int2 own = rows_range(br, a.nblk, own0, own1 - own0);
+    for (int base = lo; base < hi; base += 64) {
+      int c = base + lane;
+      bool miss = false;
+      if (c < hi) {
+        int2 o = rows_range(br, a.nblk, c * a.other_rows, a.other_rows);
+        miss = o.y < own.x || o.x > own.y;
+      }
+      if (__ballot(miss)) {
+        sparse = true;
+        break;
+      }
+    }
+  }
+  if (lane == 0) a.out[wid] = make_int2(lo | (sparse ? kRangeSparse : 0), hi);
 }
 
 // ---------------------------------------------------------------------------

@@ -2,6 +2,7 @@
 // by the attention kernels.
 #pragma once
 #include "common.hpp"
+#include "kernels.hpp"
 
 namespace bwattn {
 
@@ -249,6 +250,14 @@ struct TileWalk {
   }
   __device__ void next() { seek(t); }
 };
+
+// Set a walk's range from a range-table entry: the per-tile segment test
+// (blk) is kept only for ranges marked sparse.
+__device__ __forceinline__ void walk_range(TileWalk& w, int2 r, const int2* blk) {
+  w.lo = r.x & (kRangeSparse - 1);
+  w.hi = r.y;
+  w.blk = (r.x & kRangeSparse) ? blk : nullptr;
+}
 
 // Software pipeline over the tile walk with an NSTAGE ring of LDS buffers
 // (ring[i] = base + i * stride), in one of two orders:

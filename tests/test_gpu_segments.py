@@ -1,0 +1,54 @@
+"""Segment ids that are not contiguous (the packing mask is equality of ids:
+zhao9797 page "LWM (Large World Model)", 训练方法).  Ids change per 64-row
+tile so that a block's range of candidate tiles contains tiles of other
+segments: the walks must test each tile there, while for contiguous
+segments every tile in the range is useful.  Forward and backward, bf16 and
+fp32 paths, against the oracle."""
+import numpy as np
+import pytest
+
+from helpers import assert_parity, to64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+# segment id of each 64-row tile
+TILE_IDS = [0, 0, 0, 0, 7, 7, 0, 0, 3, 3, 0, 0, 7, 7, 0, 3, 3, 7]
+
+
+@pytest.mark.parametrize("path", ["bf16", "f32"])
+@pytest.mark.parametrize("causal,kv_chunk", [(False, 0), (True, 0), (False, 256)])
+def test_interleaved_segments(oracle, torch_cuda, path, causal, kv_chunk):
+    import long_context_blockwise_attn_amd as bw
+    from long_context_blockwise_attn_amd.inputs import random_case
+
+    torch = torch_cuda
+    S = 64 * len(TILE_IDS) - 17  # ragged last tile
+    B, H, D = 1, 2, 128
+    f32 = path == "f32"
+    (q, k, v, do), _, pos = random_case(B, H, S, D, seed=S + causal, dtype="fp32" if f32 else "bf16")
+    seg = np.repeat(np.array(TILE_IDS, dtype=np.int32), 64)[:S][None]
+    print("interleaved segments %s S%d causal %d chunk %d" % (path, S, causal, kv_chunk), flush=True)
+    fwd, bwd = (bw.attn_fwd_f32, bw.attn_bwd_f32) if f32 else (bw.attn_fwd, bw.attn_bwd)
+    dseg, dpos = torch.from_numpy(seg).cuda(), torch.from_numpy(pos).cuda()
+    qc, kc, vc, doc = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    o, lse = fwd(qc, kc, vc, dseg, dpos, theta=1e6, causal=causal, kv_chunk=kv_chunk)
+    dq, dk, dv = bwd(qc, kc, vc, o, lse, doc, dseg, dpos, theta=1e6, causal=causal, kv_chunk=kv_chunk)
+    torch.cuda.synchronize()
+    bars = dict(max_abs=2e-4, mean_abs=2e-5) if f32 else {}
+    ro, rlse = oracle.attn_fwd(to64(q), to64(k), to64(v), seg, pos, theta=1e6, causal=causal)
+    rdq, rdk, rdv = oracle.attn_bwd(to64(q), to64(k), to64(v), to64(do), seg, pos, theta=1e6, causal=causal)
+    assert_parity(to64(o), ro, "O", **bars)
+    assert_parity(lse.cpu().numpy(), rlse, "LSE", **bars)
+    assert_parity(to64(dq), rdq, "dq", **bars)
+    assert_parity(to64(dk), rdk, "dk", **bars)
+    assert_parity(to64(dv), rdv, "dv", **bars)
