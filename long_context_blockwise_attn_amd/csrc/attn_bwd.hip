@@ -328,6 +328,10 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
       const char* qtl = buf;
       const char* dtl = buf + QT::kBytes;
       const float* st = (const float*)(buf + SB);
+      // the per-lane LDS offsets are re-formed per tile: kept live across the
+      // loop they would be spilled, and their reload's vmcnt wait would also
+      // wait for the next tile's loads
+      const int ln = opaque(lane);
       const bool need_mask = seg_mask || (i0 + BQT > S) || (a.causal && i0 < j0 + 31);
 #pragma unroll
       for (int qg = 0; qg < 2; ++qg) {
@@ -335,8 +339,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int dc = 0; dc < NDC; ++dc) {
-          bf16x8 qa = QT::read(qtl, 32 * qg, dc, lane);
-          bf16x8 da = QT::read(dtl, 32 * qg, dc, lane);
+          bf16x8 qa = QT::read(qtl, 32 * qg, dc, ln);
+          bf16x8 da = QT::read(dtl, 32 * qg, dc, ln);
           s = mfma32(qa, kop[dc], s);
           dp = mfma32(da, vop[dc], dp);
         }
@@ -383,8 +387,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
           for (int dg = 0; dg < NDG; ++dg) {
             // dO^T and Q^T from the row tiles: rows 32 qg + 16 c .. in the
             // order pk[c] and dsk[c] hold them
-            bf16x8 dta = QT::read_tr(dtl, 32 * qg + 16 * c, 32 * dg, lane);
-            bf16x8 qta = QT::read_tr(qtl, 32 * qg + 16 * c, 32 * dg, lane);
+            bf16x8 dta = QT::read_tr(dtl, 32 * qg + 16 * c, 32 * dg, ln);
+            bf16x8 qta = QT::read_tr(qtl, 32 * qg + 16 * c, 32 * dg, ln);
             dv[dg] = mfma32(dta, pk[c], dv[dg]);
             dk[dg] = mfma32(qta, dsk[c], dk[dg]);
           }

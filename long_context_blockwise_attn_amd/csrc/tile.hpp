@@ -49,6 +49,14 @@ struct PTile {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
+// x, hidden from the optimizer (an empty asm statement that emits no
+// instruction): addresses derived from it inside a loop body are formed again
+// in each iteration instead of being kept live, and spilled, across the loop.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // A value the caller knows to be the same in every lane, held in a scalar
 // register so that branches on it are wave-level jumps.
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
