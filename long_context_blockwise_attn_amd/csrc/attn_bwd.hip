@@ -210,7 +210,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
       }
     }
   };
-  run_pipeline<NSTAGE, false>(walk, per_tile, smem, BUF, load, compute);
+  run_pipeline<NSTAGE, true>(walk, per_tile, smem, BUF, load, compute);
 
   if (ok) {
     if (a.rope) {
@@ -409,7 +409,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
 }
 
 hipError_t launch_attn_bwd_dq(const BwdArgs& a, int D, hipStream_t st) {
-  constexpr int NW = 8, NSTAGE = 2;
+  constexpr int NW = 8, NSTAGE = 3;
   dim3 grid((unsigned)((int64_t)a.B * a.H * a.n_qtiles)), block(NW * 64);
   if (D == 128)
     hipLaunchKernelGGL((attn_bwd_dq_kernel<128, NW, NSTAGE>), grid, block, 0, st, a);
