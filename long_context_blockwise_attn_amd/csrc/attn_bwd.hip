@@ -69,7 +69,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
   constexpr int BQ = kFwdBlockQ, BK = kFwdBlockK;
   static_assert(BQ == NW * 32, "one 32-row group per wave");
   constexpr int NDC = D / 16, NDG = D / 32;
-  using KT = PTile<BK, D / 8, 2>;  // K and V rows (K^T read transposed)
+  using KT = PTile<BK, D / 8, 3>;  // K and V rows (K^T read transposed)
   constexpr int SEG_OFF = 2 * KT::kBytes;  // segment ids of the tile's keys
   constexpr int BUF = SEG_OFF + 256;
   // ring of [K, V, seg] stages (see run_pipeline)
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
   const float sl2 = a.scale_log2;
   const uint16_t* kh = a.k + base;
   const uint16_t* vh = a.v + base;
-  TileFill<BK, D / 8, NW, 2> rfill;  // K and V rows
+  TileFill<BK, D / 8, NW, 3> rfill;  // K and V rows
   rfill.init(D * 2, tid);
   auto load = [&](int t, char* buf) {
     const uint32_t rbytes = (uint32_t)min(S - t * BK, BK) * D * 2;  // rows past S read zero
@@ -231,7 +231,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
   constexpr int BKV = kBwdBlockK, BQT = kBwdBlockQ;
   static_assert(BKV == NW * 32, "one 32-key group per wave");
   constexpr int NDC = D / 16, NDG = D / 32;
-  using QT = PTile<BQT, D / 8, 2>;  // Q and dO rows (Q^T, dO^T read transposed)
+  using QT = PTile<BQT, D / 8, 3>;  // Q and dO rows (Q^T, dO^T read transposed)
   constexpr int SB = 2 * QT::kBytes;  // row statistics: -LSE log2e [64], -Delta [64], seg [64]
   constexpr int BUF = SB + 3 * 256;
   // ring of [Q, dO, statistics] stages (see run_pipeline)
@@ -299,7 +299,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
 
   // tiles of a Q block and its row statistics (-LSE log2(e), -Delta,
   // segment id), the statistics fetched by wave 0
-  TileFill<BQT, D / 8, NW, 2> rfill;  // Q and dO rows
+  TileFill<BQT, D / 8, NW, 3> rfill;  // Q and dO rows
   rfill.init(D * 2, tid);
   auto load = [&](int t, char* buf) {
     const uint32_t rbytes = (uint32_t)min(S - t * BQT, BQT) * D * 2;  // rows past S read zero

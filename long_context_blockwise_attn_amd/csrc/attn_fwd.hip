@@ -36,7 +36,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   constexpr int NDG = D / 32;  // 32-row groups of O^T over D
   constexpr float kLazy = 8.f;
   using KT = PTile<BK, D / 8>;  // K rows
-  using VR = PTile<BK, D / 8, 2>;  // V rows (V^T read transposed)
+  // V rows (V^T read transposed).  P = 4 would make these reads conflict-free
+  // but measured no faster: its two extra pad chunks per row lengthen the loads.
+  using VR = PTile<BK, D / 8, 2>;
   constexpr int SEG_OFF = KT::kBytes + VR::kBytes;  // segment ids of the tile's keys
   constexpr int BUF = SEG_OFF + 256;
   __shared__ __attribute__((aligned(16))) char smem[NSTAGE * BUF];

@@ -7,13 +7,17 @@
 namespace bwattn {
 
 // An LDS tile of R rows x C 16-byte chunks (8 bf16 each), row-major with P
-// chunks of padding per row.  With P = 1 (row stride (C+1)*16 bytes), the
-// 16-byte reads of 16 consecutive rows at one chunk land on 16 distinct
-// 16-byte bank groups (64 banks of 4 bytes), and 8 consecutive rows on 8
-// distinct groups of a 32-bank layout, so the MFMA operand reads below are
-// conflict-free, and a lane's reads at different chunks differ by immediate
-// offsets.  P = 2 keeps that and also spreads the transposing reads of
-// tr_operand over every bank exactly twice (P = 1 hits some four times).
+// chunks of padding per row (row stride (C+P)*16 bytes); a lane's reads at
+// different chunks differ by immediate offsets.  The LDS serves a 16-byte
+// read 16 lanes at a time over 256 bytes of banks, and a ds_read_b64_tr_b16
+// 32 lanes at a time, which here means 4 rows x 64 bytes.  So read (below)
+// is conflict-free when C + P is odd (16 consecutive rows fall on 16
+// distinct 16-byte bank groups), and read_tr when the stride is 64 modulo
+// 128 bytes (the 4 rows fall on distinct quarters of the banks); no padding
+// gives both.  Measured on gfx950 at C = 16: P = 1 or 3 run the 16-byte
+// reads at full rate and P = 2 or 4 at half rate; P = 4 runs the
+// transposing reads at full rate, P = 2 or 3 at half and P = 1 at a quarter.
+// The backward's tiles, read both ways, take P = 3.
 template <int R, int C, int P = 1>
 struct PTile {
   static constexpr int kChunks = C;
