@@ -156,3 +156,18 @@ def test_packed_ce_full_workload(oracle, torch_cuda):
     assert excess.max() <= 1e-30, float(excess.max())
     print("  loss %.6f (oracle %.6f), max ce error %.2e over %d rows" % (float(loss.item()), rl, err_ce, S),
           flush=True)
+
+
+def test_packed_ce_rows_packed_differently(oracle, torch_cuda):
+    """Two batch rows with different example boundaries: an example is
+    (batch row, segment id), so the counts and weights are per row."""
+    from long_context_blockwise_attn_amd.inputs import ce_targets
+
+    rows = [[100, 150, 50], [20, 200, 80]]
+    V = 4096
+    parts = [ce_targets(r, V, seed=53 + i) for i, r in enumerate(rows)]
+    tg = np.concatenate([p[0] for p in parts])
+    seg = np.concatenate([p[1] for p in parts])
+    x = np.random.default_rng(59).standard_normal((len(rows), seg.shape[1], V), dtype=np.float32) * 3
+    got = run_gpu(torch_cuda, x, tg, seg, 3)
+    check_against_oracle(oracle, got, x, tg, seg, 3)
