@@ -75,7 +75,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
   // ring of [K, V, seg] stages (see run_pipeline)
   __shared__ __attribute__((aligned(16))) char smem[NSTAGE * BUF];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
   const int hl = lane >> 5, l32 = lane & 31;
   int bh, rank;
   xcd_tile_order(blockIdx.x, a.B * a.H, a.n_qtiles, bh, rank);
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
     if (use_seg && w == 0) row64_to_lds(segb, t * BK, S, buf + SEG_OFF, lane);
   };
   const int per_tile = 2 * rfill.count() + (use_seg && w == 0 ? 1 : 0);
-  auto compute = [&](int t, const char* buf) {
+  auto compute = [&](int t, const char* buf, auto&& issue) {
     const int k0 = t * BK;
     bool skip = q0 >= S || (a.causal && k0 > qlast);
     bool seg_mask = false;
@@ -163,6 +163,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
       else
         seg_mask = !(kr.x == kr.y && wrange.x == wrange.y && kr.x == wrange.x);
     }
+    if (uniform(skip)) issue();  // a skipped tile still issues this wave's loads
     if (!skip) {
       const char* ktl = buf;
       const char* vtl = buf + KT::kBytes;
@@ -207,10 +208,11 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
         lds_mfma_pipe<2 * NDG, 6>(
             [&](int i) { return KT::read_tr(ktl, 32 * kg + 16 * (i / NDG), 32 * (i % NDG), lane); },
             [&](int i, bf16x8 x) { dq[i % NDG] = mfma32(x, dsk[i / NDG], dq[i % NDG]); });
+        if (kg == 0) issue();  // the loads of tile t + 2, between the two halves
       }
     }
   };
-  run_pipeline<NSTAGE, true>(walk, per_tile, smem, BUF, load, compute);
+  run_pipeline_mid<NSTAGE>(walk, per_tile, smem, BUF, load, compute);
 
   if (ok) {
     if (a.rope) {
@@ -237,7 +239,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
   // ring of [Q, dO, statistics] stages (see run_pipeline)
   __shared__ __attribute__((aligned(16))) char smem[NSTAGE * BUF];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
   const int hl = lane >> 5, l32 = lane & 31;
   int bh, rank;
   xcd_tile_order(blockIdx.x, a.B * a.H, a.n_bkv, bh, rank);
@@ -267,6 +269,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
   const int segk = (use_seg && jok) ? segb[j] : 0;
   int2 wrange = make_int2(0, 0);
   if (use_seg && j0 < S) wrange = seg_range(blkb, a.nblk, j0, min(32, S - j0));
+  wrange = make_int2(uniform(wrange.x), uniform(wrange.y));
 
   TileWalk walk;
   if (a.krange) {
@@ -312,7 +315,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
     }
   };
   const int per_tile = 2 * rfill.count() + (w == 0 ? (use_seg ? 3 : 2) : 0);
-  auto compute = [&](int t, const char* buf) {
+  auto compute = [&](int t, const char* buf, auto&& issue) {
     const int i0 = t * BQT;
     const int ilast = min(S - 1, i0 + BQT - 1);
     bool skip = j0 >= S || (a.causal && ilast < j0);
@@ -324,6 +327,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
       else
         seg_mask = !(qr.x == qr.y && wrange.x == wrange.y && qr.x == wrange.x);
     }
+    if (uniform(skip)) issue();  // a skipped tile still issues this wave's loads
     if (!skip) {
       const char* qtl = buf;
       const char* dtl = buf + QT::kBytes;
@@ -393,10 +397,11 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
             dk[dg] = mfma32(qta, dsk[c], dk[dg]);
           }
         }
+        if (qg == 0) issue();  // the loads of tile t + 2, between the two halves
       }
     }
   };
-  run_pipeline<NSTAGE, true>(walk, per_tile, smem, BUF, load, compute);
+  run_pipeline_mid<NSTAGE>(walk, per_tile, smem, BUF, load, compute);
 
   if (jok) {
     if (a.rope) {

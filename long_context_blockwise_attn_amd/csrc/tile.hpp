@@ -323,4 +323,47 @@ __device__ __forceinline__ void run_pipeline(TileWalk walk, int per_tile, char* 
   }
 }
 
+// As run_pipeline<NSTAGE, true>, but the loads of tile t + NSTAGE - 1 (into
+// the slot of tile t - 1, free since the last barrier) go out from inside
+// compute(t, buf, issue), which calls issue() exactly once per tile, at a
+// point of its choosing: a wave that issues between its own MFMA phases
+// takes the load path's stall while the other wave of its SIMD keeps the
+// matrix unit busy.
+template <int NSTAGE, class Load, class Compute>
+__device__ __forceinline__ void run_pipeline_mid(TileWalk walk, int per_tile, char* base, int stride, Load&& load,
+                                                 Compute&& compute) {
+  static_assert(NSTAGE >= 3, "the slot of tile t - 1 takes tile t + NSTAGE - 1");
+  TileWalk ahead = walk;
+  int issued = 0;
+  if (walk.t >= 0) load(uniform(walk.t), base);
+  for (int st = 1; st < NSTAGE - 1; ++st) {
+    if (ahead.t >= 0) ahead.next();
+    if (ahead.t >= 0) {
+      load(uniform(ahead.t), base + st * stride);
+      ++issued;
+    }
+  }
+  wait_vmem_le(issued * per_tile);
+  __syncthreads();
+  int cur = 0;
+  auto issue_next = [&]() {
+    if (ahead.t >= 0) ahead.next();
+    if (ahead.t >= 0) {
+      const int fill = cur == 0 ? NSTAGE - 1 : cur - 1;
+      load(uniform(ahead.t), base + fill * stride);
+      ++issued;
+    }
+  };
+  while (walk.t >= 0) {
+    TileWalk nx = walk;
+    nx.next();
+    compute(uniform(walk.t), (const char*)(base + cur * stride), issue_next);
+    if (nx.t >= 0) --issued;
+    wait_vmem_le(issued * per_tile);
+    __syncthreads();
+    cur = cur + 1 == NSTAGE ? 0 : cur + 1;
+    walk = nx;
+  }
+}
+
 }  // namespace bwattn
