@@ -234,8 +234,9 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
   static_assert(BKV == NW * 32, "one 32-key group per wave");
   constexpr int NDC = D / 16, NDG = D / 32;
   using QT = PTile<BQT, D / 8, 3>;  // Q and dO rows (Q^T, dO^T read transposed)
-  constexpr int SB = 2 * QT::kBytes;  // row statistics: -LSE log2e [64], -Delta [64], seg [64]
-  constexpr int BUF = SB + 3 * 256;
+  constexpr int SB = 2 * QT::kBytes;  // row statistics: -LSE log2e [BQT], -Delta [BQT], seg [BQT]
+  constexpr int BUF = SB + 3 * 4 * BQT;
+  static_assert(BQT == 128, "statistics fetched as two 64-row runs");
   // ring of [Q, dO, statistics] stages (see run_pipeline)
   __shared__ __attribute__((aligned(16))) char smem[NSTAGE * BUF];
 
@@ -279,9 +280,13 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
     walk.hi = a.n_bq;
     walk.blk = nullptr;
   }
-  walk.ct = a.chunk_tiles;  // a chunk of kv_chunk rows is kv_chunk / 64 tiles on both sides
-  walk.nc = a.chunk_tiles ? (a.n_bq + a.chunk_tiles - 1) / a.chunk_tiles : 1;
-  walk.r = a.chunk_tiles ? (K0 / BQT) / a.chunk_tiles : 0;
+  // ring order over chunks of kv_chunk rows, counted in whole tiles of BQT
+  // rows (rounded down: a kv_chunk of 64 rows walks in natural order, an odd
+  // multiple of 64 in chunks one half tile short; every tile is visited once)
+  const int ctq = a.chunk_tiles * kFwdBlockK / BQT;
+  walk.ct = ctq;  // a chunk of kv_chunk rows is kv_chunk / 64 tiles on both sides
+  walk.nc = ctq ? (a.n_bq + ctq - 1) / ctq : 1;
+  walk.r = ctq ? (K0 / BQT) / ctq : 0;
   walk.dir = +1;
   // natural order: from the last query tile down, so that workgroups of one
   // head stream the same Q/dO tiles at the same time (L2 reuse)
@@ -308,13 +313,19 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
     const uint32_t rbytes = (uint32_t)min(S - t * BQT, BQT) * D * 2;  // rows past S read zero
     rfill.fill(qh + (int64_t)t * BQT * D, rbytes, buf);
     rfill.fill(dh + (int64_t)t * BQT * D, rbytes, buf + QT::kBytes);
+    // statistics: wave 0 -LSE log2e, wave 1 -Delta, wave 2 the segment ids
     if (w == 0) {
       row64_to_lds(nlse_h, t * BQT, S, buf + SB, lane);
-      row64_to_lds(ndel_h, t * BQT, S, buf + SB + 256, lane);
-      if (use_seg) row64_to_lds(segb, t * BQT, S, buf + SB + 512, lane);
+      row64_to_lds(nlse_h, min(t * BQT + 64, S), S, buf + SB + 256, lane);
+    } else if (w == 1) {
+      row64_to_lds(ndel_h, t * BQT, S, buf + SB + 4 * BQT, lane);
+      row64_to_lds(ndel_h, min(t * BQT + 64, S), S, buf + SB + 4 * BQT + 256, lane);
+    } else if (w == 2 && use_seg) {
+      row64_to_lds(segb, t * BQT, S, buf + SB + 8 * BQT, lane);
+      row64_to_lds(segb, min(t * BQT + 64, S), S, buf + SB + 8 * BQT + 256, lane);
     }
   };
-  const int per_tile = 2 * rfill.count() + (w == 0 ? (use_seg ? 3 : 2) : 0);
+  const int per_tile = 2 * rfill.count() + ((w == 0 || w == 1 || (w == 2 && use_seg)) ? 2 : 0);
   auto compute = [&](int t, const char* buf, auto&& issue) {
     const int i0 = t * BQT;
     const int ilast = min(S - 1, i0 + BQT - 1);
@@ -338,7 +349,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
       const int ln = opaque(lane);
       const bool need_mask = seg_mask || (i0 + BQT > S) || (a.causal && i0 < j0 + 31);
 #pragma unroll
-      for (int qg = 0; qg < 2; ++qg) {
+      for (int qg = 0; qg < BQT / 32; ++qg) {
         // S[i][j] and dP[i][j] for rows i = i0 + 32 qg + 8 (r/4) + 4 hl + r%4
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
@@ -353,7 +364,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
           for (int r = 0; r < 16; ++r) {
             int ri = 32 * qg + 8 * (r >> 2) + 4 * hl + (r & 3);
             int i = i0 + ri;
-            int sq = ((const int*)st)[128 + ri];
+            int sq = ((const int*)st)[2 * BQT + ri];
             bool vis = i < S && (!a.causal || j <= i) && (!use_seg || sq == segk);
             s[r] = vis ? s[r] : kNegInf;
           }
@@ -369,7 +380,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
             const int rq = 2 * c + hq;
             const int ri = 32 * qg + 8 * rq + 4 * hl;
             const f32x4 nl = *(const f32x4*)(st + ri);
-            const f32x4 nd = *(const f32x4*)(st + 64 + ri);
+            const f32x4 nd = *(const f32x4*)(st + BQT + ri);
             float pv[4], dsv[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -397,7 +408,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
             dk[dg] = mfma32(qta, dsk[c], dk[dg]);
           }
         }
-        if (qg == 0) issue();  // the loads of tile t + 2, between the two halves
+        if (qg == BQT / 64 - 1) issue();  // the loads of tile t + 1, in the middle of the tile
       }
     }
   };
@@ -424,7 +435,7 @@ hipError_t launch_attn_bwd_dq(const BwdArgs& a, int D, hipStream_t st) {
 }
 
 hipError_t launch_attn_bwd_dkdv(const BwdArgs& a, int D, hipStream_t st) {
-  constexpr int NW = 8, NSTAGE = 3;
+  constexpr int NW = 8, NSTAGE = 2;
   dim3 grid((unsigned)((int64_t)a.B * a.H * a.n_bkv)), block(NW * 64);
   if (D == 128)
     hipLaunchKernelGGL((attn_bwd_dkdv_kernel<128, NW, NSTAGE>), grid, block, 0, st, a);

@@ -426,7 +426,7 @@ void attn_bwd_dq_f32_kernel(F32Args a) {
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_bwd_dkdv_f32_kernel(F32Args a) {
-  constexpr int BKV = kF32BwdBlockK, BQT = kBwdBlockQ;
+  constexpr int BKV = kF32BwdBlockK, BQT = kF32BwdBlockQ;
   static_assert(BKV == NW * 32, "32 keys per wave");
   constexpr int NC = D / 8, R = D / 32;
   using T = FTile<BQT, D>;

@@ -111,7 +111,8 @@ Plan make_plan(const attn_params* p, int which, bool f32) {
   pl.n_qtiles = (pl.S + pl.bq - 1) / pl.bq;
   pl.n_ktiles = (pl.S + kFwdBlockK - 1) / kFwdBlockK;
   pl.n_bkv = (pl.S + pl.bkv - 1) / pl.bkv;
-  pl.n_bq = (pl.S + kBwdBlockQ - 1) / kBwdBlockQ;
+  const int bqo = f32 ? kF32BwdBlockQ : kBwdBlockQ;
+  pl.n_bq = (pl.S + bqo - 1) / bqo;
   const size_t esize = f32 ? 4 : 2;
   size_t n = (size_t)pl.B * pl.H * pl.S * pl.D;
   size_t off = 0;
@@ -217,7 +218,7 @@ int prepare(const attn_params* p, const Plan& pl, const void* q, const void* k, 
       // key tiles -> query tile ranges (dK/dV)
       t.out = (int2*)(ws + pl.off_krange);
       t.own_rows = pl.bkv;
-      t.other_rows = kBwdBlockQ;
+      t.other_rows = pl.f32 ? kF32BwdBlockQ : kBwdBlockQ;
       t.n_own = pl.n_bkv;
       t.n_other = pl.n_bq;
       t.own_is_query = 0;

@@ -9,7 +9,8 @@ namespace bwattn {
 constexpr int kFwdBlockQ = 256;   // query rows per forward / dQ workgroup (8 waves x 32 rows)
 constexpr int kFwdBlockK = 64;    // keys per K/V tile streamed by the forward / dQ kernels
 constexpr int kBwdBlockK = 256;   // keys per dK/dV workgroup (8 waves x 32 keys)
-constexpr int kBwdBlockQ = 64;    // query rows per Q/dO tile streamed by the dK/dV kernel
+constexpr int kBwdBlockQ = 128;   // query rows per Q/dO tile streamed by the bf16 dK/dV kernel
+constexpr int kF32BwdBlockQ = 64;  // query rows per Q/dO tile streamed by the fp32 dK/dV kernel
 constexpr int kSegBlock = 32;     // rows per segment-range block
 
 struct RopeArgs {

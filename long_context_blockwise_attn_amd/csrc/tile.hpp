@@ -332,7 +332,7 @@ __device__ __forceinline__ void run_pipeline(TileWalk walk, int per_tile, char* 
 template <int NSTAGE, class Load, class Compute>
 __device__ __forceinline__ void run_pipeline_mid(TileWalk walk, int per_tile, char* base, int stride, Load&& load,
                                                  Compute&& compute) {
-  static_assert(NSTAGE >= 3, "the slot of tile t - 1 takes tile t + NSTAGE - 1");
+  static_assert(NSTAGE >= 2, "the slot of tile t - 1 takes tile t + NSTAGE - 1");
   TileWalk ahead = walk;
   int issued = 0;
   if (walk.t >= 0) load(uniform(walk.t), base);
