@@ -12,10 +12,14 @@
 //
 // Two kernels, no atomics (the result is bitwise reproducible):
 //  - dQ kernel: a workgroup owns 256 query rows (like the forward) and
-//    streams K/V tiles; it also forms Delta for its rows.  3 contractions per
-//    tile pair (S, dP, dQ).
+//    streams K/V tiles of 64 keys (three-slot ring); it also forms Delta for
+//    its rows.  3 contractions per tile pair (S, dP, dQ).
 //  - dK/dV kernel: a workgroup owns kBwdBlockK keys and streams Q/dO tiles of
-//    64 rows.  4 contractions per tile pair (S, dP, dV, dK).
+//    kBwdBlockQ rows (two-slot ring).  4 contractions per tile pair (S, dP,
+//    dV, dK).
+// Each wave issues its share of the next tile's loads between the 32-row (or
+// 32-key) halves of the tile it computes, where its issue stall overlaps
+// the MFMAs of the other wave of its SIMD.
 // Operands with k along the sequence (K^T for dQ, Q^T and dO^T for dK/dV)
 // are read from the same row tiles with transposing LDS reads
 // (PTile::read_tr), so each tile is loaded once and no transposed copy is
