@@ -72,8 +72,8 @@ typedef struct {
   int32_t kv_chunk;      /* 0: K/V blocks visited in natural order.  > 0: ring order: the    */
                          /* sequence is cut in chunks of kv_chunk keys (a multiple of 64);   */
                          /* queries of chunk r visit chunk r, r-1, ..., 0, C-1, ..., r+1.    */
-                         /* (attn_bwd's dK/dV pass walks query tiles of 128 rows: its chunks */
-                         /* are rounded down to whole tiles; the result is the same sum.)    */
+                         /* (attn_bwd walks tiles of 128 rows or keys: its chunks are        */
+                         /* rounded down to whole tiles; the result is the same sum.)        */
   int32_t deterministic; /* reserved, must be 0 or 1; 1 asks attn_bwd for a bitwise          */
                          /* reproducible result (no float atomics)                           */
 } attn_params;

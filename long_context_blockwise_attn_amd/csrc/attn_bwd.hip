@@ -12,7 +12,7 @@
 //
 // Two kernels, no atomics (the result is bitwise reproducible):
 //  - dQ kernel: a workgroup owns 256 query rows (like the forward) and
-//    streams K/V tiles of 64 keys (three-slot ring); it also forms Delta for
+//    streams K/V tiles of 128 keys (two-slot ring); it also forms Delta for
 //    its rows.  3 contractions per tile pair (S, dP, dQ).
 //  - dK/dV kernel: a workgroup owns kBwdBlockK keys and streams Q/dO tiles of
 //    kBwdBlockQ rows (two-slot ring).  4 contractions per tile pair (S, dP,
@@ -70,12 +70,12 @@ __device__ __forceinline__ void store_rows(uint16_t* dst_row, const f32x16 (&x)[
 // ---------------------------------------------------------------------------
 template <int D, int NW, int NSTAGE>
 __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
-  constexpr int BQ = kFwdBlockQ, BK = kFwdBlockK;
+  constexpr int BQ = kFwdBlockQ, BK = 2 * kFwdBlockK;  // two tiles of the K/V range table per tile
   static_assert(BQ == NW * 32, "one 32-row group per wave");
   constexpr int NDC = D / 16, NDG = D / 32;
   using KT = PTile<BK, D / 8, 3>;  // K and V rows (K^T read transposed)
   constexpr int SEG_OFF = 2 * KT::kBytes;  // segment ids of the tile's keys
-  constexpr int BUF = SEG_OFF + 256;
+  constexpr int BUF = SEG_OFF + 4 * BK;
   // ring of [K, V, seg] stages (see run_pipeline)
   __shared__ __attribute__((aligned(16))) char smem[NSTAGE * BUF];
 
@@ -124,16 +124,24 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
   if (use_seg && q0 < S) wrange = seg_range(blkb, a.nblk, q0, min(32, S - q0));
 
   TileWalk walk;
+  const int nk = (S + BK - 1) / BK;  // K/V tiles of BK keys
   if (a.qrange) {
+    // the range table counts tiles of kFwdBlockK keys; a tile of BK keys that
+    // holds a useful one is useful, so a dense range stays dense
     walk_range(walk, a.qrange[(int64_t)b * a.n_qtiles + qt], blkb);
+    walk.lo = walk.lo * kFwdBlockK / BK;
+    walk.hi = min(nk, (walk.hi * kFwdBlockK + BK - 1) / BK);
   } else {
     walk.lo = 0;
-    walk.hi = a.causal ? min(a.n_ktiles, (min(S, Q0 + BQ) - 1) / BK + 1) : a.n_ktiles;
+    walk.hi = a.causal ? min(nk, (min(S, Q0 + BQ) - 1) / BK + 1) : nk;
     walk.blk = nullptr;
   }
-  walk.ct = a.chunk_tiles;
-  walk.nc = a.chunk_tiles ? (a.n_ktiles + a.chunk_tiles - 1) / a.chunk_tiles : 1;
-  walk.r = a.chunk_tiles ? (Q0 / BK) / a.chunk_tiles : 0;
+  // ring order over chunks of kv_chunk keys, counted in whole tiles of BK
+  // keys (rounded down; every tile is visited once either way)
+  const int ctk = a.chunk_tiles * kFwdBlockK / BK;
+  walk.ct = ctk;
+  walk.nc = ctk ? (nk + ctk - 1) / ctk : 1;
+  walk.r = ctk ? (Q0 / BK) / ctk : 0;
   walk.dir = -1;
   walk.desc = false;
   walk.nblk = a.nblk;
@@ -153,9 +161,12 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
     const uint32_t rbytes = (uint32_t)min(S - t * BK, BK) * D * 2;  // rows past S read zero
     rfill.fill(kh + (int64_t)t * BK * D, rbytes, buf);
     rfill.fill(vh + (int64_t)t * BK * D, rbytes, buf + KT::kBytes);
-    if (use_seg && w == 0) row64_to_lds(segb, t * BK, S, buf + SEG_OFF, lane);
+    if (use_seg && w == 0) {
+      row64_to_lds(segb, t * BK, S, buf + SEG_OFF, lane);
+      row64_to_lds(segb, min(t * BK + 64, S), S, buf + SEG_OFF + 256, lane);
+    }
   };
-  const int per_tile = 2 * rfill.count() + (use_seg && w == 0 ? 1 : 0);
+  const int per_tile = 2 * rfill.count() + (use_seg && w == 0 ? 2 : 0);
   auto compute = [&](int t, const char* buf, auto&& issue) {
     const int k0 = t * BK;
     bool skip = q0 >= S || (a.causal && k0 > qlast);
@@ -174,7 +185,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
       const int* segk_lds = (const int*)(buf + SEG_OFF);
       const bool need_mask = seg_mask || (k0 + BK > S) || (a.causal && k0 + BK - 1 > q0);
 #pragma unroll
-      for (int kg = 0; kg < 2; ++kg) {
+      for (int kg = 0; kg < BK / 32; ++kg) {
         // dP^T starts from -Delta, so the MFMAs leave dP^T - Delta
         f32x16 s = f32x16{}, dp;
 #pragma unroll
@@ -212,7 +223,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
         lds_mfma_pipe<2 * NDG, 6>(
             [&](int i) { return KT::read_tr(ktl, 32 * kg + 16 * (i / NDG), 32 * (i % NDG), lane); },
             [&](int i, bf16x8 x) { dq[i % NDG] = mfma32(x, dsk[i / NDG], dq[i % NDG]); });
-        if (kg == 0) issue();  // the loads of tile t + 2, between the two halves
+        if (kg == BK / 64 - 1) issue();  // the loads of tile t + 1, in the middle of the tile
       }
     }
   };
@@ -429,7 +440,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
 }
 
 hipError_t launch_attn_bwd_dq(const BwdArgs& a, int D, hipStream_t st) {
-  constexpr int NW = 8, NSTAGE = 3;
+  constexpr int NW = 8, NSTAGE = 2;
   dim3 grid((unsigned)((int64_t)a.B * a.H * a.n_qtiles)), block(NW * 64);
   if (D == 128)
     hipLaunchKernelGGL((attn_bwd_dq_kernel<128, NW, NSTAGE>), grid, block, 0, st, a);
