@@ -118,6 +118,15 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
     a.ndelta[(int64_t)bh * S + row] = -delta;
     a.nlse2[(int64_t)bh * S + row] = nlse2;
   }
+  // start values of the S^T and dP^T MFMAs: the query operand carries
+  // scale * log2(e), so S^T starts from -LSE log2(e) and leaves the exponent
+  // of exp2; dP^T starts from -Delta and leaves dP^T - Delta
+  f32x16 s_init, dp_init;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    s_init[r] = nlse2;
+    dp_init[r] = -delta;
+  }
   const int segq = (use_seg && ok) ? segb[row] : 0;
   const int qlast = min(S - 1, q0 + 31);
   int2 wrange = make_int2(0, 0);
@@ -152,7 +161,6 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
   f32x16 dq[NDG];
 #pragma unroll
   for (int dg = 0; dg < NDG; ++dg) dq[dg] = f32x16{};
-  const float sl2 = a.scale_log2;
   const uint16_t* kh = a.k + base;
   const uint16_t* vh = a.v + base;
   TileFill<BK, D / 8, NW, 3> rfill;  // K and V rows
@@ -186,10 +194,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
       const bool need_mask = seg_mask || (k0 + BK > S) || (a.causal && k0 + BK - 1 > q0);
 #pragma unroll
       for (int kg = 0; kg < BK / 32; ++kg) {
-        // dP^T starts from -Delta, so the MFMAs leave dP^T - Delta
-        f32x16 s = f32x16{}, dp;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) dp[r] = -delta;
+        f32x16 s = s_init, dp = dp_init;
         lds_mfma_pipe<2 * NDC, 6>(
             [&](int i) { return KT::read((i & 1) ? vtl : ktl, 32 * kg, i >> 1, lane); },
             [&](int i, bf16x8 x) {
@@ -210,7 +215,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
         }
         bf16x8 dsk[2];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = fast_exp2(__builtin_fmaf(s[r], sl2, nlse2)) * dp[r];
+        for (int r = 0; r < 16; ++r) s[r] = fast_exp2(s[r]) * dp[r];
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           int r0 = 8 * c;
@@ -314,7 +319,6 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
   f32x16 dk[NDG], dv[NDG];
 #pragma unroll
   for (int dg = 0; dg < NDG; ++dg) dk[dg] = dv[dg] = f32x16{};
-  const float sl2 = a.scale_log2;
   const uint16_t* qh = a.q + base;
   const uint16_t* dh = a.dout + base;
   const float* nlse_h = a.nlse2 + (int64_t)bh * S;
@@ -365,8 +369,22 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
       const bool need_mask = seg_mask || (i0 + BQT > S) || (a.causal && i0 < j0 + 31);
 #pragma unroll
       for (int qg = 0; qg < BQT / 32; ++qg) {
-        // S[i][j] and dP[i][j] for rows i = i0 + 32 qg + 8 (r/4) + 4 hl + r%4
-        f32x16 s = f32x16{}, dp = f32x16{};
+        // S[i][j] and dP[i][j] for rows i = i0 + 32 qg + 8 (r/4) + 4 hl + r%4.
+        // The MFMAs start from the rows' statistics: S (whose query operand
+        // carries scale * log2(e)) from -LSE log2(e), dP from -Delta, so they
+        // leave the exponent of exp2 and dP - Delta
+        f32x16 s, dp;
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int ri = 32 * qg + 8 * rq + 4 * hl;
+          const f32x4 nl = *(const f32x4*)(st + ri);
+          const f32x4 nd = *(const f32x4*)(st + BQT + ri);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            s[4 * rq + e] = nl[e];
+            dp[4 * rq + e] = nd[e];
+          }
+        }
 #pragma unroll
         for (int dc = 0; dc < NDC; ++dc) {
           bf16x8 qa = QT::read(qtl, 32 * qg, dc, ln);
@@ -384,8 +402,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
             s[r] = vis ? s[r] : kNegInf;
           }
         }
-        // P = exp(S scale - LSE) and dS = P (dP - Delta); the statistics of
-        // each 4 rows are read from LDS where they are used
+        // P = exp(S scale - LSE) and dS = P (dP - Delta)
         bf16x8 pk[2], dsk[2];
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
@@ -393,14 +410,11 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
           for (int hq = 0; hq < 2; ++hq) {
             const int rq = 2 * c + hq;
-            const int ri = 32 * qg + 8 * rq + 4 * hl;
-            const f32x4 nl = *(const f32x4*)(st + ri);
-            const f32x4 nd = *(const f32x4*)(st + BQT + ri);
             float pv[4], dsv[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              pv[e] = fast_exp2(__builtin_fmaf(s[4 * rq + e], sl2, nl[e]));
-              dsv[e] = pv[e] * (dp[4 * rq + e] + nd[e]);
+              pv[e] = fast_exp2(s[4 * rq + e]);
+              dsv[e] = pv[e] * dp[4 * rq + e];
             }
             pw[2 * hq] = pack_bf16x2(pv[0], pv[1]);
             pw[2 * hq + 1] = pack_bf16x2(pv[2], pv[3]);
@@ -434,7 +448,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
       double pos = a.pos ? (double)a.pos[(int64_t)b * S + j] : (double)j;
       rope_backward_row<NDG>(dk, pos, a.turns, hl);
     }
-    store_rows<D>(a.dk + base + (int64_t)j * D, dk, a.scale, hl);
+    store_rows<D>(a.dk + base + (int64_t)j * D, dk, a.dk_scale, hl);  // Q^T dS used the scaled query rows
     store_rows<D>(a.dv + base + (int64_t)j * D, dv, 1.f, hl);
   }
 }

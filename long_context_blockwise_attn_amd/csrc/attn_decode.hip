@@ -102,7 +102,6 @@ __global__ __launch_bounds__(64) void attn_decode_partial_kernel(DecodeArgs a) {
   f32x16 o[NDG];
 #pragma unroll
   for (int dg = 0; dg < NDG; ++dg) o[dg] = f32x16{};
-  const float sl2 = a.scale_log2;
   constexpr float kLazy = 8.f;
 
   bf16x8 kc_[NDC], vc_[NV];
@@ -117,7 +116,8 @@ __global__ __launch_bounds__(64) void attn_decode_partial_kernel(DecodeArgs a) {
       load_k(t0 + TK, kn);
       load_v(t0 + TK, vn);
     }
-    // S^T: s[i] holds key t0 + 8 (i/4) + 4 hl + i%4 of this lane's row
+    // S^T in log2 units (the query rows carry scale * log2(e)): s[i] holds
+    // key t0 + 8 (i/4) + 4 hl + i%4 of this lane's row
     f32x16 s = f32x16{};
 #pragma unroll
     for (int dc = 0; dc < NDC; ++dc) s = mfma32(kc_[dc], qop[dc], s);
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(64) void attn_decode_partial_kernel(DecodeArgs a) {
     float mx = s[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
-    mx = pair_max(mx) * sl2;
+    mx = pair_max(mx);
     const bool grow = mx > m + kLazy;
     if (__ballot(grow)) {
       const float mnew = grow ? fmaxf(m, mx) : m;
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(64) void attn_decode_partial_kernel(DecodeArgs a) {
     for (int kc = 0; kc < 2; ++kc) {
       float p[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) p[e] = fast_exp2(__builtin_fmaf(s[8 * kc + e], sl2, -muse));
+      for (int e = 0; e < 8; ++e) p[e] = fast_exp2(s[8 * kc + e] - muse);
       u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                   pack_bf16x2(p[6], p[7])};
 #pragma unroll

@@ -8,7 +8,9 @@
 // the packing mask (each packed example attends only to itself, 训练方法).
 //
 // Work decomposition: a workgroup of NW waves owns 256 query rows of one
-// (batch, head); each wave owns 32 rows.  Tiles of 64 keys of K and V rows sit
+// (batch, head); each wave owns 32 rows.  The query rows arrive multiplied by
+// scale * log2(e) and the score MFMAs start from -m, the row's running max,
+// so they leave scale * log2(e) * <q', k'> - m, the exponent of exp2 itself.  Tiles of 64 keys of K and V rows sit
 // in an NSTAGE-deep LDS ring filled by buffer-to-LDS loads.  Scores are
 // computed transposed, S^T = K Q^T, so each lane holds one query row: the row
 // max needs one exchange between lanes l and l^32, and the running rescale of
@@ -92,11 +94,11 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   walk.own = use_seg ? seg_range(blkb, a.nblk, Q0, min(BQ, S - Q0)) : make_int2(0, 0);
   walk.start();
 
-  float m = kNegInf, lsum = 0.f;
+  float m = kNegInf, lsum = 0.f;  // running max (log2 units) and sum
+  f32x16 negm = f32x16{};          // -m in every register (0 while m = -inf)
   f32x16 o[NDG];
 #pragma unroll
   for (int dg = 0; dg < NDG; ++dg) o[dg] = f32x16{};
-  const float sl2 = a.scale_log2;
 
   const uint16_t* kh = a.k + base;
   const uint16_t* vh = a.v + base;
@@ -114,9 +116,10 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   const int per_tile = kfill.count() + vfill.count() + (use_seg && w == 0 ? 1 : 0);
 
   // --- per-tile pieces -----------------------------------------------------
-  // S^T of the tile in `buf`: s[kg] holds keys k0 + 32 kg + 8 (r/4) + 4 hl + r%4
+  // S^T - m of the tile in `buf` (log2 units): s[kg] holds keys
+  // k0 + 32 kg + 8 (r/4) + 4 hl + r%4
   auto scores = [&](const char* buf, f32x16 (&s)[2]) {
-    s[0] = s[1] = f32x16{};
+    s[0] = s[1] = negm;
     lds_mfma_pipe<2 * NDC, 3>([&](int i) { return KT::read(buf, 32 * (i & 1), i >> 1, lane); },
                               [&](int i, bf16x8 x) { s[i & 1] = mfma32(x, qop[i >> 1], s[i & 1]); });
   };
@@ -146,41 +149,50 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
         }
     }
   };
-  // Row max of a tile's raw scores, in log2 units of the scaled scores.
+  // Row max of a tile's scores, relative to m (to 0 while m = -inf).
   auto tile_max = [&](const f32x16 (&s)[2]) {
     float mx = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(fmaxf(mx, s[0][r]), s[1][r]);
-    return pair_max(mx) * sl2;
+    return pair_max(mx);
   };
   // Lazy online-softmax max update.  A row's running max m is raised only
   // when its new max exceeds it by more than kLazy (log2 units); otherwise
   // the stale m stays, p <= 2^kLazy, and O is not touched.  l and O share m,
   // so the normalised result is unchanged.  The decision is per row (the
   // wave only branches when some row needs it), so a row's result depends on
-  // its own visible keys alone.
-  auto rescale = [&](float mx) {
-    const bool grow = mx > m + kLazy;
+  // its own visible keys alone.  A raised m moves the tile's scores by the
+  // rise and the start value of later tiles' score MFMAs with it.
+  auto rescale = [&](float mx, f32x16 (&s)[2]) {
+    const bool grow = mx > (m == kNegInf ? kNegInf : kLazy);
     if (__ballot(grow)) {
-      float mnew = grow ? fmaxf(m, mx) : m;
-      float alpha = fast_exp2(m - (mnew == kNegInf ? 0.f : mnew));  // 1 when m stays
+      const float rise = grow ? mx : 0.f;
+      const float mnew = grow ? (m == kNegInf ? mx : m + mx) : m;
+      const float alpha = fast_exp2(grow ? m - mnew : 0.f);  // 0 from m = -inf, where l and O are 0
       lsum *= alpha;
 #pragma unroll
       for (int dg = 0; dg < NDG; ++dg) o[dg] *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[0][r] -= rise;
+        s[1][r] -= rise;
+      }
       m = mnew;
+      const float nm = (m == kNegInf) ? 0.f : -m;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) negm[r] = nm;
     }
   };
   // P = 2^(S*scale*log2e - m) as bf16 MFMA operands pk[kc] (keys 16 kc ..),
   // and the row sum over the same bf16 values
   auto softmax = [&](const f32x16 (&s)[2], bf16x8 (&pk)[4]) {
-    const float muse = (m == kNegInf) ? 0.f : m;
     float rs = lsum;
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
       const int r0 = 8 * (kc & 1);
       float p[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) p[e] = fast_exp2(__builtin_fmaf(s[kc >> 1][r0 + e], sl2, -muse));
+      for (int e = 0; e < 8; ++e) p[e] = fast_exp2(s[kc >> 1][r0 + e]);
       u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                   pack_bf16x2(p[6], p[7])};
 #pragma unroll
@@ -237,7 +249,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
       f32x16 s0[2];
       scores(slot(0), s0);
       mask(uniform(walk.t), slot(0), s0);
-      rescale(tile_max(s0));
+      rescale(tile_max(s0), s0);
       softmax(s0, pk);
     }
     if (grp == 1) __syncthreads();  // G_1: group 1 starts one phase later
@@ -267,7 +279,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
         refill(k);
       if (more) {
         mask(uniform(w1.t), slot(k + 1), s_next);
-        rescale(tile_max(s_next));
+        rescale(tile_max(s_next), s_next);
         softmax(s_next, pk);
       }
       if (grp == 0)

@@ -116,9 +116,13 @@ Plan make_plan(const attn_params* p, int which, bool f32) {
   const size_t esize = f32 ? 4 : 2;
   size_t n = (size_t)pl.B * pl.H * pl.S * pl.D;
   size_t off = 0;
-  if (pl.rope) {
+  // rotated rows; the bf16 path always keeps its query rows here, rotated or
+  // not, times scale * log2(e)
+  if (pl.rope || !f32) {
     pl.off_qr = off;
     off += align256(n * esize);
+  }
+  if (pl.rope) {
     pl.off_kr = off;
     off += align256(n * esize);
   }
@@ -168,10 +172,14 @@ float scale_of(const attn_params* p) {
   return p->softmax_scale > 0.f ? p->softmax_scale : (float)(1.0 / std::sqrt((double)p->head_dim));
 }
 
-// RoPE of q and k into the workspace, and the segment schedule.
+float scale_log2_of(const attn_params* p) { return scale_of(p) * 1.4426950408889634f; }
+
+// RoPE of q and k into the workspace, and the segment schedule.  The bf16
+// path stores its query rows times scale * log2(e) (rotated or not), so the
+// score MFMAs of its kernels leave scores in log2 units.
 int prepare(const attn_params* p, const Plan& pl, const void* q, const void* k, const int32_t* seg,
             const int32_t* pos, char* ws, bool bwd, hipStream_t st) {
-  if (pl.rope) {
+  if (pl.rope || !pl.f32) {
     RopeArgs r{};
     r.pos = pos;
     r.B = pl.B;
@@ -179,16 +187,18 @@ int prepare(const attn_params* p, const Plan& pl, const void* q, const void* k, 
     r.S = pl.S;
     r.D = pl.D;
     r.inverse = 0;
-    fill_turns(r.turns, pl.D, p->rope_theta);
+    if (pl.rope) fill_turns(r.turns, pl.D, p->rope_theta);  // else all zero: the identity rotation
     const void* src[2] = {q, k};
     const size_t dst[2] = {pl.off_qr, pl.off_kr};
+    const float out_scale[2] = {scale_log2_of(p), 1.f};
     const char* what[2] = {"rope(q) launch", "rope(k) launch"};
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < (pl.rope ? 2 : 1); ++i) {
       int rc = hip_status(timed_launch(ATTN_KERNEL_ROPE, st,
                                        [&] {
                                          if (pl.f32) return launch_rope_f32(r, (const float*)src[i], (float*)(ws + dst[i]), st);
                                          r.x = (const uint16_t*)src[i];
                                          r.y = (uint16_t*)(ws + dst[i]);
+                                         r.out_scale = out_scale[i];
                                          return launch_rope(r, st);
                                        }),
                           what[i]);
@@ -253,7 +263,8 @@ F32Args f32_args(const attn_params* p, const Plan& pl, const void* q, const void
   return a;
 }
 
-// Decode workspace: rotated query rows, then the chunk states.  About 2048
+// Decode workspace: the query rows (rotated or not) times scale * log2(e),
+// then the chunk states.  About 2048
 // waves (8 per CU) keep enough K/V bytes in flight to cover HBM latency; a
 // chunk is a multiple of kDecodeTile keys, at least 256 (unless the cache is
 // shorter) and at most kDecodeMaxChunk.
@@ -275,7 +286,7 @@ DecodePlan make_decode_plan(const attn_params* p, int n_q) {
   d.n_chunks = (int)((S + chunk - 1) / chunk);
   size_t off = 0;
   d.off_qr = off;
-  if (p->rope_theta > 0.0) off += align256((size_t)bh * n_q * p->head_dim * 2);
+  off += align256((size_t)bh * n_q * p->head_dim * 2);
   d.off_po = off;
   off += align256((size_t)bh * d.n_chunks * n_q * p->head_dim * 4);
   d.off_ml = off;
@@ -376,6 +387,7 @@ int rope_apply(const attn_params* p, const void* x, void* y, const int32_t* posi
   r.S = p->seqlen;
   r.D = p->head_dim;
   r.inverse = inverse;
+  r.out_scale = 1.f;
   fill_turns(r.turns, p->head_dim, p->rope_theta);
   hipStream_t st = (hipStream_t)stream;
   rc = hip_status(timed_launch(ATTN_KERNEL_ROPE, st, [&] { return launch_rope(r, st); }), "rope launch");
@@ -404,7 +416,7 @@ int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, 
   rc = prepare(p, pl, q, k, segment_ids, positions, ws, false, st);
   if (rc) return rc;
   FwdArgs a{};
-  a.q = pl.rope ? (const uint16_t*)(ws + pl.off_qr) : (const uint16_t*)q;
+  a.q = (const uint16_t*)(ws + pl.off_qr);
   a.k = pl.rope ? (const uint16_t*)(ws + pl.off_kr) : (const uint16_t*)k;
   a.v = (const uint16_t*)v;
   a.o = (uint16_t*)o;
@@ -418,7 +430,6 @@ int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, 
   a.n_qtiles = pl.n_qtiles;
   a.n_ktiles = pl.n_ktiles;
   a.nblk = pl.nblk;
-  a.scale_log2 = scale_of(p) * 1.4426950408889634f;
   a.causal = p->causal;
   a.chunk_tiles = p->kv_chunk / kFwdBlockK;
   rc = hip_status(timed_launch(ATTN_KERNEL_FWD, st, [&] { return launch_attn_fwd(a, pl.D, st); }), "attn_fwd launch");
@@ -448,7 +459,7 @@ int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v, 
   rc = prepare(p, pl, q, k, segment_ids, positions, ws, true, st);
   if (rc) return rc;
   BwdArgs a{};
-  a.q = pl.rope ? (const uint16_t*)(ws + pl.off_qr) : (const uint16_t*)q;
+  a.q = (const uint16_t*)(ws + pl.off_qr);
   a.k = pl.rope ? (const uint16_t*)(ws + pl.off_kr) : (const uint16_t*)k;
   a.v = (const uint16_t*)v;
   a.o = (const uint16_t*)o;
@@ -473,7 +484,7 @@ int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v, 
   a.n_bkv = pl.n_bkv;
   a.n_bq = pl.n_bq;
   a.scale = scale_of(p);
-  a.scale_log2 = a.scale * 1.4426950408889634f;
+  a.dk_scale = (float)((double)a.scale / (double)scale_log2_of(p));
   a.causal = p->causal;
   a.chunk_tiles = p->kv_chunk / kFwdBlockK;
   a.rope = pl.rope ? 1 : 0;
@@ -618,8 +629,8 @@ int attn_decode(const attn_params* p, int32_t n_q, const void* q, const void* k_
   if (rc) return rc;
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
-  const bool rope = p->rope_theta > 0.0;
-  if (rope) {
+  {
+    // query rows times scale * log2(e), as the forward takes them
     RopeArgs r{};
     r.x = (const uint16_t*)q;
     r.y = (uint16_t*)(ws + dp.off_qr);
@@ -630,12 +641,13 @@ int attn_decode(const attn_params* p, int32_t n_q, const void* q, const void* k_
     r.S = n_q;
     r.D = p->head_dim;
     r.inverse = 0;
-    fill_turns(r.turns, p->head_dim, p->rope_theta);
+    r.out_scale = scale_log2_of(p);
+    if (p->rope_theta > 0.0) fill_turns(r.turns, p->head_dim, p->rope_theta);  // else the identity rotation
     rc = hip_status(timed_launch(ATTN_KERNEL_ROPE, st, [&] { return launch_rope(r, st); }), "rope(q) launch");
     if (rc) return rc;
   }
   DecodeArgs a{};
-  a.q = rope ? (const uint16_t*)(ws + dp.off_qr) : (const uint16_t*)q;
+  a.q = (const uint16_t*)(ws + dp.off_qr);
   a.k = (const uint16_t*)k_cache;
   a.v = (const uint16_t*)v_cache;
   a.part_o = (float*)(ws + dp.off_po);
@@ -648,7 +660,6 @@ int attn_decode(const attn_params* p, int32_t n_q, const void* q, const void* k_
   a.n_q = n_q;
   a.n_chunks = dp.n_chunks;
   a.chunk = dp.chunk;
-  a.scale_log2 = scale_of(p) * 1.4426950408889634f;
   a.causal = p->causal;
   rc = hip_status(timed_launch(ATTN_KERNEL_DECODE, st, [&] { return launch_attn_decode_partial(a, p->head_dim, st); }),
                   "attn_decode partial launch");

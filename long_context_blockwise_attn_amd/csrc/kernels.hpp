@@ -20,6 +20,7 @@ struct RopeArgs {
   int pos_base;
   int B, H, S, D;
   int inverse;
+  float out_scale;   // y = (R x) * out_scale, rounded once to bf16
   double turns[64];  // theta^(-2i/D) / (2 pi), i < D/2
 };
 
@@ -40,7 +41,7 @@ struct TileRangeArgs {
 // Forward and dQ kernels: a workgroup owns kFwdBlockQ query rows of one (b,h)
 // and streams K/V tiles of kFwdBlockK keys.
 struct FwdArgs {
-  const uint16_t* q;  // rotated queries [B,H,S,D]
+  const uint16_t* q;  // rotated queries times scale * log2(e) [B,H,S,D]
   const uint16_t* k;  // rotated keys
   const uint16_t* v;
   uint16_t* o;
@@ -50,13 +51,12 @@ struct FwdArgs {
   const int2* qrange;  // [B, n_qtiles] K/V tile range, or null
   int B, H, S;
   int n_qtiles, n_ktiles, nblk;
-  float scale_log2;    // softmax scale * log2(e)
   int causal;
   int chunk_tiles;     // ring chunk in K/V tiles; 0 = natural order
 };
 
 struct BwdArgs {
-  const uint16_t* q;   // rotated queries
+  const uint16_t* q;   // rotated queries times scale * log2(e), as in the forward
   const uint16_t* k;   // rotated keys
   const uint16_t* v;
   const uint16_t* o;
@@ -76,7 +76,7 @@ struct BwdArgs {
   int n_qtiles, n_ktiles, nblk;
   int n_bkv, n_bq;     // dK/dV kernel: key tiles of kBwdBlockK and query tiles of kBwdBlockQ
   float scale;         // softmax scale
-  float scale_log2;
+  float dk_scale;      // scale / (scale log2 e): dK' from the scaled query rows
   int causal;
   int chunk_tiles;
   int rope;            // apply the RoPE backward
@@ -91,7 +91,7 @@ constexpr int kDecodeMaxRows = 32;  // query rows per (b,h) in one decode call
 constexpr int kDecodeMaxChunk = 1 << 20;  // keys per chunk at most
 
 struct DecodeArgs {
-  const uint16_t* q;  // rotated query rows [B,H,n_q,D]
+  const uint16_t* q;  // rotated query rows times scale * log2(e) [B,H,n_q,D]
   const uint16_t* k;  // key cache [B,H,S,D] (rotated by the caller)
   const uint16_t* v;  // value cache [B,H,S,D]
   float* part_o;      // [B,H,n_chunks,n_q,D] unnormalised partial outputs
@@ -100,7 +100,6 @@ struct DecodeArgs {
   float* lse;         // [B,H,n_q], natural log
   int B, H, S, n_q;
   int n_chunks, chunk;  // chunk: keys per chunk, a multiple of kDecodeTile
-  float scale_log2;
   int causal;
 };
 

@@ -42,6 +42,9 @@ __device__ __forceinline__ int64_t rope_group(const RopeArgs& a, float (&c)[4], 
   return ((int64_t)b * a.H * a.S + s) * a.D + 8 * g;
 }
 
+// bf16 rows: y = bf16((R x) * out_scale).  The attention kernels take the
+// query rows with out_scale = softmax scale * log2(e), so their score MFMAs
+// leave scores in log2 units; keys and rope_apply use 1 (a plain rotation).
 __global__ void rope_kernel(RopeArgs a) {
   float c[4], sn[4];
   int64_t off = rope_group(a, c, sn);
@@ -55,7 +58,7 @@ __global__ void rope_kernel(RopeArgs a) {
       float x0 = bf16_lo(x[i]), x1 = bf16_hi(x[i]);
       float y0 = x0 * c[i] - x1 * sn[i];
       float y1 = x0 * sn[i] + x1 * c[i];
-      y[i] = pack_bf16x2(y0, y1);
+      y[i] = pack_bf16x2(y0 * a.out_scale, y1 * a.out_scale);
     }
     *(u32x4*)(a.y + off) = y;
   }

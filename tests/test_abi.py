@@ -177,14 +177,14 @@ def test_decode_split_is_chunks_of_tiles(lib):
     for B, H, S in ((1, 32, 1 << 20), (1, 2, 1000), (2, 1, 300), (1, 32, 32), (16, 64, 1 << 22)):
         p = bw.make_params(B, H, S, 128, theta=0.0)
         n = bw.decode_workspace_bytes(p, 1)
-        # no rotated-q block without RoPE: partial O (D floats) + (m, l), each 256-byte aligned
-        per_chunk_o, per_chunk_ml = B * H * 128 * 4, B * H * 2 * 4
+        # the scaled query row (bf16), partial O (D floats) + (m, l), each 256-byte aligned
+        q_rows, per_chunk_o, per_chunk_ml = B * H * 128 * 2, B * H * 128 * 4, B * H * 2 * 4
         al = lambda x: (x + 255) // 256 * 256
         # ... and at most 2^20 keys per chunk
         want = max(min(max(1, -(-2048 // (B * H))), max(1, -(-S // 256))), -(-S // (1 << 20)))
         chunk = -(-(-(-S // want)) // 32) * 32
         nc = -(-S // chunk)
-        assert n == al(nc * per_chunk_o) + al(nc * per_chunk_ml), (B, H, S, n, nc)
+        assert n == al(q_rows) + al(nc * per_chunk_o) + al(nc * per_chunk_ml), (B, H, S, n, nc)
 
 
 def test_packed_ce_argument_errors_before_any_hip_call(lib):
