@@ -149,12 +149,18 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
         }
     }
   };
-  // Row max of a tile's scores, relative to m (to 0 while m = -inf).
+  // Row max of a tile's scores, relative to m (to 0 while m = -inf), in four
+  // independent chains: with the other wave of the SIMD issuing MFMAs, one
+  // dependent chain of 16 steps left this wave idle between them.
   auto tile_max = [&](const f32x16 (&s)[2]) {
-    float mx = fmaxf(s[0][0], s[1][0]);
+    float mc[4];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(fmaxf(mx, s[0][r]), s[1][r]);
-    return pair_max(mx);
+    for (int c = 0; c < 4; ++c) mc[c] = fmaxf(s[c >> 1][8 * (c & 1)], s[c >> 1][8 * (c & 1) + 1]);
+#pragma unroll
+    for (int e = 2; e < 8; e += 2)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) mc[c] = fmaxf(fmaxf(mc[c], s[c >> 1][8 * (c & 1) + e]), s[c >> 1][8 * (c & 1) + e + 1]);
+    return pair_max(fmaxf(fmaxf(mc[0], mc[1]), fmaxf(mc[2], mc[3])));
   };
   // Lazy online-softmax max update.  A row's running max m is raised only
   // when its new max exceeds it by more than kLazy (log2 units); otherwise
@@ -184,11 +190,12 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
     }
   };
   // P = 2^(S*scale*log2e - m) as bf16 MFMA operands pk[kc] (keys 16 kc ..),
-  // and the row sum over the same bf16 values
+  // and the row sum over the same bf16 values (one chain per kc)
   auto softmax = [&](const f32x16 (&s)[2], bf16x8 (&pk)[4]) {
-    float rs = lsum;
+    float rsc[4] = {lsum, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
+      float rs = rsc[kc];
       const int r0 = 8 * (kc & 1);
       float p[8];
 #pragma unroll
@@ -197,9 +204,10 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
                   pack_bf16x2(p[6], p[7])};
 #pragma unroll
       for (int e = 0; e < 4; ++e) rs = dot2_bf16(pw[e], kBf16OnePair, rs);
+      rsc[kc] = rs;
       pk[kc] = __builtin_bit_cast(bf16x8, pw);
     }
-    lsum = rs;
+    lsum = (rsc[0] + rsc[1]) + (rsc[2] + rsc[3]);
   };
   auto pv = [&](const char* buf, const bf16x8 (&pk)[4]) {
     // V^T operand for keys 16 kc .. 16 kc + 15 (the keys of pk[kc]) and d 32 dg ..
