@@ -8,9 +8,10 @@
 // the packing mask (each packed example attends only to itself, 训练方法).
 //
 // Work decomposition: a workgroup of NW waves owns 256 query rows of one
-// (batch, head); each wave owns 32 rows.  The query rows arrive multiplied by
-// scale * log2(e) and the score MFMAs start from -m, the row's running max,
-// so they leave scale * log2(e) * <q', k'> - m, the exponent of exp2 itself.  Tiles of 64 keys of K and V rows sit
+// (batch, head); each wave owns 32 rows.  Each lane rotates its query row
+// (RoPE) and multiplies it by scale * log2(e) as it loads it, and the score
+// MFMAs start from -m, the row's running max, so they leave
+// scale * log2(e) * <q', k'> - m, the exponent of exp2 itself.  Tiles of 64 keys of K and V rows sit
 // in an NSTAGE-deep LDS ring filled by buffer-to-LDS loads.  Scores are
 // computed transposed, S^T = K Q^T, so each lane holds one query row: the row
 // max needs one exchange between lanes l and l^32, and the running rescale of
@@ -60,14 +61,25 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   const int32_t* segb = use_seg ? a.seg + (int64_t)b * S : nullptr;
   const int2* blkb = use_seg ? a.blk + (int64_t)b * a.nblk : nullptr;
 
-  // Q operand (B of S^T = K Q^T): lane holds row `row`, d = 16 dc + 8 hl + [0,8)
+  // Q operand (B of S^T = K Q^T): lane holds row `row`, d = 16 dc + 8 hl + [0,8),
+  // that is the pairs 8 dc + 4 hl + [0,4), rotated to the row's position and
+  // times scale * log2(e) (the same bits the RoPE pre-pass writes)
   bf16x8 qop[NDC];
   {
-    const uint16_t* src = a.q + base + (int64_t)min(row, S - 1) * D + 8 * hl;
+    const int r = min(row, S - 1);
+    const uint16_t* src = a.q + base + (int64_t)r * D + 8 * hl;
+    const double pos = a.pos ? (double)a.pos[(int64_t)b * S + r] : (double)r;
 #pragma unroll
     for (int dc = 0; dc < NDC; ++dc) {
-      bf16x8 v = *(const bf16x8*)(src + 16 * dc);
-      qop[dc] = row < S ? v : bf16x8{};
+      const u32x4 x = *(const u32x4*)(src + 16 * dc);
+      u32x4 y;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float c, s;
+        rope_cos_sin(pos, a.turns[8 * dc + 4 * hl + e], c, s);
+        y[e] = rope_pair(x[e], c, s, a.q_scale);
+      }
+      qop[dc] = row < S ? __builtin_bit_cast(bf16x8, y) : bf16x8{};
     }
   }
   const int segq = (use_seg && row < S) ? segb[row] : 0;

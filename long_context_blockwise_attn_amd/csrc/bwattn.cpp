@@ -116,9 +116,9 @@ Plan make_plan(const attn_params* p, int which, bool f32) {
   const size_t esize = f32 ? 4 : 2;
   size_t n = (size_t)pl.B * pl.H * pl.S * pl.D;
   size_t off = 0;
-  // rotated rows; the bf16 path always keeps its query rows here, rotated or
-  // not, times scale * log2(e)
-  if (pl.rope || !f32) {
+  // rotated rows; the bf16 backward always keeps its query rows here, rotated
+  // or not, times scale * log2(e) (the bf16 forward forms them as it loads)
+  if (f32 ? pl.rope : which == 1) {
     pl.off_qr = off;
     off += align256(n * esize);
   }
@@ -175,11 +175,13 @@ float scale_of(const attn_params* p) {
 float scale_log2_of(const attn_params* p) { return scale_of(p) * 1.4426950408889634f; }
 
 // RoPE of q and k into the workspace, and the segment schedule.  The bf16
-// path stores its query rows times scale * log2(e) (rotated or not), so the
-// score MFMAs of its kernels leave scores in log2 units.
+// backward stores its query rows times scale * log2(e) (rotated or not), so
+// the score MFMAs of its kernels leave scores in log2 units; the bf16 forward
+// forms those rows itself and needs only the keys.
 int prepare(const attn_params* p, const Plan& pl, const void* q, const void* k, const int32_t* seg,
             const int32_t* pos, char* ws, bool bwd, hipStream_t st) {
-  if (pl.rope || !pl.f32) {
+  const bool q_rows = pl.f32 ? pl.rope : bwd;  // query rows into the workspace
+  if (q_rows || pl.rope) {
     RopeArgs r{};
     r.pos = pos;
     r.B = pl.B;
@@ -192,7 +194,7 @@ int prepare(const attn_params* p, const Plan& pl, const void* q, const void* k, 
     const size_t dst[2] = {pl.off_qr, pl.off_kr};
     const float out_scale[2] = {scale_log2_of(p), 1.f};
     const char* what[2] = {"rope(q) launch", "rope(k) launch"};
-    for (int i = 0; i < (pl.rope ? 2 : 1); ++i) {
+    for (int i = q_rows ? 0 : 1; i < (pl.rope ? 2 : 1); ++i) {
       int rc = hip_status(timed_launch(ATTN_KERNEL_ROPE, st,
                                        [&] {
                                          if (pl.f32) return launch_rope_f32(r, (const float*)src[i], (float*)(ws + dst[i]), st);
@@ -416,7 +418,7 @@ int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, 
   rc = prepare(p, pl, q, k, segment_ids, positions, ws, false, st);
   if (rc) return rc;
   FwdArgs a{};
-  a.q = (const uint16_t*)(ws + pl.off_qr);
+  a.q = (const uint16_t*)q;
   a.k = pl.rope ? (const uint16_t*)(ws + pl.off_kr) : (const uint16_t*)k;
   a.v = (const uint16_t*)v;
   a.o = (uint16_t*)o;
@@ -432,6 +434,9 @@ int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, 
   a.nblk = pl.nblk;
   a.causal = p->causal;
   a.chunk_tiles = p->kv_chunk / kFwdBlockK;
+  a.pos = positions;
+  a.q_scale = scale_log2_of(p);
+  if (pl.rope) fill_turns(a.turns, pl.D, p->rope_theta);  // else all zero: the identity rotation
   rc = hip_status(timed_launch(ATTN_KERNEL_FWD, st, [&] { return launch_attn_fwd(a, pl.D, st); }), "attn_fwd launch");
   if (rc) return rc;
   g_err[0] = 0;

@@ -40,6 +40,27 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// RoPE of one pair (RoFormer's rotation of adjacent pairs, base theta scaled
+// with the context: zhao9797 page "LWM (Large World Model)", 模型架构).  The
+// angle pos * turns (in turns) is reduced to [-1/2, 1/2] turn in fp64 before
+// the fp32 cosine and sine: positions reach 2^20 and theta 5e7.  The RoPE
+// pre-pass and the forward's query load both go through these two functions,
+// so the forward's rotated query rows are bitwise those the backward reads.
+__device__ __forceinline__ void rope_cos_sin(double pos, double turns, float& c, float& s) {
+  double rev = pos * turns;
+  rev -= rint(rev);
+  const float f = (float)rev;
+  c = __builtin_amdgcn_cosf(f);  // cos(2 pi f)
+  s = __builtin_amdgcn_sinf(f);
+}
+// bf16 pair (x0, x1) -> bf16 pair of (R x) * scale, R the rotation by (c, s)
+__device__ __forceinline__ uint32_t rope_pair(uint32_t x, float c, float s, float scale) {
+  const float x0 = bf16_lo(x), x1 = bf16_hi(x);
+  const float y0 = x0 * c - x1 * s;
+  const float y1 = x0 * s + x1 * c;
+  return pack_bf16x2(y0 * scale, y1 * scale);
+}
+
 // Workgroup order for long-to-short scheduling with heads grouped per XCD.
 // Workgroups are handed to the 8 XCDs round robin; when the number of (b,h)
 // slices is a multiple of 8, all tiles of one slice go to one XCD so that its

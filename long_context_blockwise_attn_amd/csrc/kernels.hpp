@@ -41,7 +41,7 @@ struct TileRangeArgs {
 // Forward and dQ kernels: a workgroup owns kFwdBlockQ query rows of one (b,h)
 // and streams K/V tiles of kFwdBlockK keys.
 struct FwdArgs {
-  const uint16_t* q;  // rotated queries times scale * log2(e) [B,H,S,D]
+  const uint16_t* q;  // queries [B,H,S,D] as given (rotated and scaled on load)
   const uint16_t* k;  // rotated keys
   const uint16_t* v;
   uint16_t* o;
@@ -53,6 +53,9 @@ struct FwdArgs {
   int n_qtiles, n_ktiles, nblk;
   int causal;
   int chunk_tiles;     // ring chunk in K/V tiles; 0 = natural order
+  const int32_t* pos;  // [B,S] or null (pos = s), for the query rows' RoPE
+  float q_scale;       // softmax scale * log2(e), folded into the query rows
+  double turns[64];    // theta^(-2i/D) / (2 pi); all zero without RoPE
 };
 
 struct BwdArgs {

@@ -32,11 +32,7 @@ __device__ __forceinline__ int64_t rope_group(const RopeArgs& a, float (&c)[4], 
   double pos = a.pos ? (double)a.pos[bs] : (double)(a.pos_base + s);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    double rev = pos * a.turns[4 * g + i];  // angle in turns
-    rev -= rint(rev);                       // reduce to [-1/2, 1/2] in fp64
-    float f = (float)rev;
-    c[i] = __builtin_amdgcn_cosf(f);       // cos(2*pi*f)
-    sn[i] = __builtin_amdgcn_sinf(f);
+    rope_cos_sin(pos, a.turns[4 * g + i], c[i], sn[i]);
     if (a.inverse) sn[i] = -sn[i];
   }
   return ((int64_t)b * a.H * a.S + s) * a.D + 8 * g;
@@ -44,7 +40,8 @@ __device__ __forceinline__ int64_t rope_group(const RopeArgs& a, float (&c)[4], 
 
 // bf16 rows: y = bf16((R x) * out_scale).  The attention kernels take the
 // query rows with out_scale = softmax scale * log2(e), so their score MFMAs
-// leave scores in log2 units; keys and rope_apply use 1 (a plain rotation).
+// leave scores in log2 units (the forward forms them itself, with the same
+// functions, as it loads its query rows); keys and rope_apply use 1.
 __global__ void rope_kernel(RopeArgs a) {
   float c[4], sn[4];
   int64_t off = rope_group(a, c, sn);
@@ -54,12 +51,7 @@ __global__ void rope_kernel(RopeArgs a) {
     u32x4 x = *(const u32x4*)(a.x + off);
     u32x4 y;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float x0 = bf16_lo(x[i]), x1 = bf16_hi(x[i]);
-      float y0 = x0 * c[i] - x1 * sn[i];
-      float y1 = x0 * sn[i] + x1 * c[i];
-      y[i] = pack_bf16x2(y0 * a.out_scale, y1 * a.out_scale);
-    }
+    for (int i = 0; i < 4; ++i) y[i] = rope_pair(x[i], c[i], sn[i], a.out_scale);
     *(u32x4*)(a.y + off) = y;
   }
 }
