@@ -135,7 +135,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
     lds_mfma_pipe<2 * NDC, 3>([&](int i) { return KT::read(buf, 32 * (i & 1), i >> 1, lane); },
                               [&](int i, bf16x8 x) { s[i & 1] = mfma32(x, qop[i >> 1], s[i & 1]); });
   };
-  // causal / segment / sequence-end mask of tile t (wave-uniform decision)
+  // causal / segment / sequence-end mask of tile t.  The decisions are
+  // wave-uniform, and a tile tests only what it needs: the position limit
+  // (diagonal, sequence end), the segment ids (document edge), or both.
   auto mask = [&](int t, const char* buf, f32x16 (&s)[2]) {
     const int k0 = t * BK;
     bool seg_mask = false;
@@ -143,22 +145,31 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
       int2 kr = seg_range(blkb, a.nblk, k0, BK);
       seg_mask = !(kr.x == kr.y && wrange.x == wrange.y && kr.x == wrange.x);
     }
-    if (seg_mask || (k0 + BK > S) || (a.causal && k0 + BK - 1 > q0)) {
+    const bool lim_mask = (k0 + BK > S) || (a.causal && k0 + BK - 1 > q0);
+    if (uniform(seg_mask || lim_mask)) {
       const int* segk = (const int*)(buf + SEG_OFF);
-      const int lim = a.causal ? min(S - 1, row) : S - 1;  // last visible key of this row
+      const int lim = (a.causal ? min(S - 1, row) : S - 1) - k0 - 4 * hl;  // last visible key, tile-relative
+      // keys k0 + 32 kg + 8 rq + 4 hl + e in registers s[kg][4 rq + e]
+      if (!uniform(seg_mask)) {
 #pragma unroll
-      for (int kg = 0; kg < 2; ++kg)
+        for (int kg = 0; kg < 2; ++kg)
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          const int jj = 32 * kg + 8 * rq + 4 * hl;  // keys jj .. jj+3 in registers 4 rq ..
-          const int4 sk = *(const int4*)(segk + jj);
-          const int sk_[4] = {sk.x, sk.y, sk.z, sk.w};
+          for (int r = 0; r < 16; ++r) s[kg][r] = (32 * kg + 8 * (r >> 2) + (r & 3) <= lim) ? s[kg][r] : kNegInf;
+      } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const bool vis = (k0 + jj + e <= lim) & (((sk_[e] ^ segq) & segsel) == 0);
-            s[kg][4 * rq + e] = vis ? s[kg][4 * rq + e] : kNegInf;
+        for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq) {
+            const int jj = 32 * kg + 8 * rq + 4 * hl;
+            const int4 sk = *(const int4*)(segk + jj);
+            const int sk_[4] = {sk.x, sk.y, sk.z, sk.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const bool vis = (uniform(lim_mask) ? (32 * kg + 8 * rq + e <= lim) : true) & (sk_[e] == segq);
+              s[kg][4 * rq + e] = vis ? s[kg][4 * rq + e] : kNegInf;
+            }
           }
-        }
+      }
     }
   };
   // Row max of a tile's scores, relative to m (to 0 while m = -inf), in four
