@@ -191,7 +191,9 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
       const char* ktl = buf;
       const char* vtl = buf + KT::kBytes;
       const int* segk_lds = (const int*)(buf + SEG_OFF);
-      const bool need_mask = seg_mask || (k0 + BK > S) || (a.causal && k0 + BK - 1 > q0);
+      const bool lim_mask = (k0 + BK > S) || (a.causal && k0 + BK - 1 > q0);
+      const bool need_mask = seg_mask || lim_mask;
+      const int lim = (a.causal ? min(S - 1, row) : S - 1) - k0 - 4 * hl;  // last visible key, tile-relative
 #pragma unroll
       for (int kg = 0; kg < BK / 32; ++kg) {
         f32x16 s = s_init, dp = dp_init;
@@ -203,14 +205,23 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
               else
                 s = mfma32(x, qop[i >> 1], s);
             });
-        if (need_mask) {
+        if (uniform(need_mask)) {
+          // key k0 + 32 kg + 8 (r/4) + 4 hl + r%4 in register r; test only
+          // what the tile needs
+          if (!uniform(seg_mask)) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            int j = k0 + 32 * kg + 8 * (r >> 2) + 4 * hl + (r & 3);
-            int sk = 0;
-            if (use_seg) sk = segk_lds[j - k0];
-            bool vis = j < S && (!a.causal || j <= row) && (!use_seg || sk == segq);
-            s[r] = vis ? s[r] : kNegInf;
+            for (int r = 0; r < 16; ++r) s[r] = (32 * kg + 8 * (r >> 2) + (r & 3) <= lim) ? s[r] : kNegInf;
+          } else {
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+              const int4 sk = *(const int4*)(segk_lds + 32 * kg + 8 * rq + 4 * hl);
+              const int sk_[4] = {sk.x, sk.y, sk.z, sk.w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const bool vis = (uniform(lim_mask) ? (32 * kg + 8 * rq + e <= lim) : true) & (sk_[e] == segq);
+                s[4 * rq + e] = vis ? s[4 * rq + e] : kNegInf;
+              }
+            }
           }
         }
         bf16x8 dsk[2];
@@ -397,8 +408,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
           for (int r = 0; r < 16; ++r) {
             int ri = 32 * qg + 8 * (r >> 2) + 4 * hl + (r & 3);
             int i = i0 + ri;
-            int sq = ((const int*)st)[2 * BQT + ri];
-            bool vis = i < S && (!a.causal || j <= i) && (!use_seg || sq == segk);
+            const bool vis = i < S && (!a.causal || j <= i) && (!seg_mask || ((const int*)st)[2 * BQT + ri] == segk);
             s[r] = vis ? s[r] : kNegInf;
           }
         }
