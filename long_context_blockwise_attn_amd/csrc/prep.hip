@@ -46,13 +46,28 @@ __global__ void rope_kernel(RopeArgs a) {
   float c[4], sn[4];
   int64_t off = rope_group(a, c, sn);
   if (off < 0) return;
+  // four heads' loads in flight per thread; every byte is read and written
+  // once, so the accesses bypass the caches' retention (non-temporal)
   const int64_t head_stride = (int64_t)a.S * a.D;
-  for (int h = 0; h < a.H; ++h, off += head_stride) {
-    u32x4 x = *(const u32x4*)(a.x + off);
+  int h = 0;
+  for (; h + 4 <= a.H; h += 4, off += 4 * head_stride) {
+    u32x4 x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x[u] = __builtin_nontemporal_load((const u32x4*)(a.x + off + u * head_stride));
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      u32x4 y;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[i] = rope_pair(x[u][i], c[i], sn[i], a.out_scale);
+      __builtin_nontemporal_store(y, (u32x4*)(a.y + off + u * head_stride));
+    }
+  }
+  for (; h < a.H; ++h, off += head_stride) {
+    u32x4 x = __builtin_nontemporal_load((const u32x4*)(a.x + off));
     u32x4 y;
 #pragma unroll
     for (int i = 0; i < 4; ++i) y[i] = rope_pair(x[i], c[i], sn[i], a.out_scale);
-    *(u32x4*)(a.y + off) = y;
+    __builtin_nontemporal_store(y, (u32x4*)(a.y + off));
   }
 }
 
