@@ -21,6 +21,7 @@ struct RopeArgs {
   int B, H, S, D;
   int inverse;
   float out_scale;   // y = (R x) * out_scale, rounded once to bf16
+  int stream;        // nonzero: the streaming variant for tensors of 512 MiB and more
   double turns[64];  // theta^(-2i/D) / (2 pi), i < D/2
 };
 
