@@ -5,9 +5,11 @@ TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
 CPU-baseline leg may import this package.  The GPU library never calls it and
 shares no code with it.
 
-The arithmetic lives in ``oracle.c`` (built to ``liboracle.so`` by ``build()``);
-this module only marshals numpy arrays.  Each function states the passage of
-the pages it follows; see the header of ``oracle.c``.
+The attention arithmetic lives in ``oracle.c`` (built to ``liboracle.so`` by
+``build()``); this module marshals numpy arrays, except for ``attn_probs``
+(the full probability and dS matrices of small cases, in numpy) and the loss
+of ``packed_ce.py``.  Each function states the passage of the pages it
+follows; see the header of ``oracle.c``.
 """
 from __future__ import annotations
 
@@ -146,6 +148,45 @@ def attn_bwd(q, k, v, dout, segment_ids=None, positions=None, theta=0.0, scale=0
                                    float(theta), float(scale), int(bool(causal)), _ptr(r), n, int(col_begin),
                                    int(col_end), _ptr(dq), _ptr(dk), _ptr(dv)))
     return dq, dk, dv
+
+
+def attn_probs(q, k, v, dout, segment_ids=None, positions=None, theta=0.0, scale=0.0, causal=True):
+    """The intermediate matrices of the exact backward, for small S (numpy,
+    float64, full S x S matrices per head).  With q', k' the rotated rows
+    (RoPE as in rope()), s_ij = scale <q'_i, k'_j> over the visible pairs
+    (causal: j <= i; packing: equal segment ids), P = softmax_j(s),
+    O = P v, Delta_i = <dO_i, O_i>, dP_ij = <dO_i, v_j> and
+    dS_ij = P_ij (dP_ij - Delta_i) (zhao9797 page, 训练方法: training takes
+    gradient steps through the exact attention of 模型架构).
+
+    Returns (P, dS, q', k'), P and dS [B,H,S,S] (zero off the mask), q' and
+    k' [B,H,S,D].  For bounds on the rounding of these operands in the
+    tests; the outputs themselves come from attn_fwd / attn_bwd."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, S, D = q.shape
+    seg, pos = _i32(segment_ids, B, S), _i32(positions, B, S)
+    if S > 4096:
+        raise ValueError("attn_probs keeps S x S matrices; S %d is too large" % S)
+    tau = scale if scale > 0 else 1.0 / np.sqrt(D)
+    qr = rope(q, pos, theta) if theta > 0 else q
+    kr = rope(k, pos, theta) if theta > 0 else k
+    P = np.zeros((B, H, S, S))
+    dS = np.zeros((B, H, S, S))
+    idx = np.arange(S)
+    for b in range(B):
+        vis = np.ones((S, S), dtype=bool) if seg is None else seg[b][:, None] == seg[b][None, :]
+        if causal:
+            vis &= idx[None, :] <= idx[:, None]
+        for h in range(H):
+            s = np.where(vis, tau * (qr[b, h] @ kr[b, h].T), -np.inf)
+            e = np.exp(s - s.max(axis=1, keepdims=True))
+            p = e / e.sum(axis=1, keepdims=True)
+            o = p @ v[b, h]
+            delta = np.sum(dout[b, h] * o, axis=1)
+            dp = dout[b, h] @ v[b, h].T
+            P[b, h] = p
+            dS[b, h] = np.where(vis, p * (dp - delta[:, None]), 0.0)
+    return P, dS, qr, kr
 
 
 # loss side of masked sequence packing (numpy, float64)

@@ -145,3 +145,26 @@ def test_row_and_column_windows(oracle):
     _, dkt, dvt = oracle.attn_bwd(q, k, v, dout, None, None, theta=1e4, rows=tail, col_begin=60, col_end=90)
     np.testing.assert_allclose(dkt, dk[:, :, 60:], atol=1e-13)
     np.testing.assert_allclose(dvt, dv[:, :, 60:], atol=1e-13)
+
+
+@pytest.mark.parametrize("n_docs,causal,theta", [(0, True, 1e6), (3, True, 1e7), (2, False, 0.0)])
+def test_probability_matrices_against_the_backward(oracle, n_docs, causal, theta):
+    """attn_probs (numpy) against the C oracle: P v = O, rows of P sum to 1,
+    rows of dS sum to 0, dv = P^T dO, dq = R(-a) scale dS k' and
+    dk = R(-a) scale dS^T q'."""
+    from long_context_blockwise_attn_amd.inputs import random_case
+
+    S, D = 150, 32
+    (q, k, v, do), seg, pos = random_case(1, 2, S, D, seed=19 + n_docs, n_docs=n_docs, dtype="fp32")
+    q, k, v, do = (x.double().numpy() for x in (q, k, v, do))
+    P, dS, qr, kr = oracle.attn_probs(q, k, v, do, seg, pos, theta=theta, causal=causal)
+    o, _ = oracle.attn_fwd(q, k, v, seg, pos, theta=theta, causal=causal)
+    dq, dk, dv = oracle.attn_bwd(q, k, v, do, seg, pos, theta=theta, causal=causal)
+    np.testing.assert_allclose(P @ v, o, atol=1e-12)
+    np.testing.assert_allclose(P.sum(-1), 1.0, atol=1e-13)
+    np.testing.assert_allclose(dS.sum(-1), 0.0, atol=1e-11)
+    np.testing.assert_allclose(np.swapaxes(P, -1, -2) @ do, dv, atol=1e-12)
+    tau = 1.0 / np.sqrt(D)
+    back = (lambda x: oracle.rope(x, pos, theta, inverse=True)) if theta > 0 else (lambda x: x)
+    np.testing.assert_allclose(back(tau * dS @ kr), dq, atol=1e-11)
+    np.testing.assert_allclose(back(tau * np.swapaxes(dS, -1, -2) @ qr), dk, atol=1e-11)
