@@ -184,13 +184,11 @@ def make_qkv(w: Workload, device="cpu", with_grad_out: bool = False, heads: int 
 
 
 def random_case(B, H, S, D, seed, n_docs=0, device="cpu", dtype="bf16"):
-    """Small random case for parity tests: q, k, v (float32 N(0,1) from numpy
-    PCG64(seed)) and dO (the same draw times 1/2, so that the gradients of
-    causal documents stay below 4 in magnitude, where a bf16 value's own
-    rounding takes at most 2^-8), kept as float32 for dtype "fp32", else
-    rounded to bf16; and, if n_docs > 0, n_docs contiguous documents of random
-    lengths (positions restart per document); otherwise one document with
-    positions 0..S-1."""
+    """Small random case for parity tests: q, k, v and dO, float32 N(0,1)
+    from numpy PCG64(seed), kept as float32 for dtype "fp32", else rounded to
+    bf16; and, if n_docs > 0, n_docs contiguous documents of random lengths
+    (positions restart per document); otherwise one document with positions
+    0..S-1."""
     import torch
 
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -202,8 +200,8 @@ def random_case(B, H, S, D, seed, n_docs=0, device="cpu", dtype="bf16"):
         seg, pos = None, np.tile(np.arange(S, dtype=np.int32), (B, 1))
     shape = (B, H, S, D)
     out_dtype = torch.float32 if dtype == "fp32" else torch.bfloat16
-    ts = [torch.from_numpy(rng.standard_normal(size=shape, dtype=np.float32) * (0.5 if i == 3 else 1.0))
-          .to(out_dtype).to(device) for i in range(4)]
+    ts = [torch.from_numpy(rng.standard_normal(size=shape, dtype=np.float32)).to(out_dtype).to(device)
+          for i in range(4)]
     return ts, seg, pos
 
 

@@ -46,9 +46,9 @@ def test_bwd_matches_oracle(oracle, torch_cuda, B, H, S, D, n_docs, causal, thet
     dq, dk, dv = bw.attn_bwd(qc, kc, vc, o, lse, doc, dseg, dpos, theta=theta, causal=causal, kv_chunk=kv_chunk)
     torch.cuda.synchronize()
     rdq, rdk, rdv = oracle.attn_bwd(to64(q), to64(k), to64(v), to64(do), seg, pos, theta=theta, causal=causal)
-    assert_parity(to64(dq), rdq, "dq")
-    assert_parity(to64(dk), rdk, "dk")
-    assert_parity(to64(dv), rdv, "dv")
+    assert_parity(dq, rdq, "dq")
+    assert_parity(dk, rdk, "dk")
+    assert_parity(dv, rdv, "dv")
 
 
 def test_bwd_deterministic_and_masks_exact(torch_cuda):
@@ -73,3 +73,65 @@ def test_bwd_deterministic_and_masks_exact(torch_cuda):
     c = bw.attn_bwd(q, k2, v2, o2, lse2, do, None, None, theta=1e6)
     torch.cuda.synchronize()
     assert torch.equal(a[0][:, :, :t + 1], c[0][:, :, :t + 1])
+
+
+def test_bwd_other_documents_are_exactly_excluded(torch_cuda):
+    """Masked sequence packing: each packed example attends only to itself
+    (zhao9797 page, 训练方法, Masked Sequence Packing), so its gradients do
+    not depend on the other examples at all.  Poisoning q, k, v and dO of
+    the other documents with large finite values leaves dq, dk and dv of the
+    middle document bitwise unchanged (forward recomputed on the poisoned
+    inputs; causal and non-causal; natural and ring order)."""
+    import long_context_blockwise_attn_amd as bw
+    from long_context_blockwise_attn_amd.inputs import segments_from_lengths
+    torch = torch_cuda
+    lengths = [333, 517, 410]  # the middle document straddles tile edges on both sides
+    S = sum(lengths)
+    seg_np, pos_np = segments_from_lengths(lengths)
+    seg, pos = torch.from_numpy(seg_np).cuda(), torch.from_numpy(pos_np).cuda()
+    g = torch.Generator(device="cuda").manual_seed(21)
+    q, k, v, do = (torch.randn(1, 2, S, 128, generator=g, device="cuda").to(torch.bfloat16) for _ in range(4))
+    a0, a1 = lengths[0], lengths[0] + lengths[1]
+    other = torch.ones(S, dtype=torch.bool, device="cuda")
+    other[a0:a1] = False
+    poisoned = []
+    for t, val in ((q, 1e3), (k, 1e4), (v, -1e4), (do, 1e4)):
+        p = t.clone()
+        p[:, :, other] = val
+        poisoned.append(p)
+    for causal, chunk in ((True, 0), (False, 0), (True, 256)):
+        print("packed poisoning causal %d chunk %d" % (causal, chunk), flush=True)
+        res = []
+        for qq, kk, vv, dd in ((q, k, v, do), tuple(poisoned)):
+            o, lse = bw.attn_fwd(qq, kk, vv, seg, pos, theta=1e7, causal=causal, kv_chunk=chunk)
+            res.append((o, lse) + bw.attn_bwd(qq, kk, vv, o, lse, dd, seg, pos, theta=1e7, causal=causal,
+                                              kv_chunk=chunk))
+        torch.cuda.synchronize()
+        for name, x, y in zip(("o", "lse", "dq", "dk", "dv"), res[0], res[1]):
+            assert torch.equal(x[:, :, a0:a1], y[:, :, a0:a1]), name
+
+
+def test_bwd_key_gradients_do_not_see_the_past(torch_cuda):
+    """Causal mask in the key gradients: key j receives gradient only from
+    query rows i >= j.  Poisoning q and dO of the rows before t leaves dk
+    and dv of every key after t bitwise unchanged."""
+    import long_context_blockwise_attn_amd as bw
+    torch = torch_cuda
+    g = torch.Generator(device="cuda").manual_seed(22)
+    B, H, S, D = 1, 2, 1300, 128
+    q, k, v, do = (torch.randn(B, H, S, D, generator=g, device="cuda").to(torch.bfloat16) for _ in range(4))
+    t = 611  # not on a tile edge
+    q2, do2 = q.clone(), do.clone()
+    q2[:, :, :t] = 1e3
+    do2[:, :, :t] = -1e4
+    for chunk in (0, 256):
+        print("causal key-gradient poisoning chunk %d" % chunk, flush=True)
+        res = []
+        for qq, dd in ((q, do), (q2, do2)):
+            o, lse = bw.attn_fwd(qq, k, v, None, None, theta=1e6, kv_chunk=chunk)
+            res.append(bw.attn_bwd(qq, k, v, o, lse, dd, None, None, theta=1e6, kv_chunk=chunk))
+        torch.cuda.synchronize()
+        assert torch.equal(res[0][1][:, :, t:], res[1][1][:, :, t:]), "dk"
+        assert torch.equal(res[0][2][:, :, t:], res[1][2][:, :, t:]), "dv"
+        # and dq of rows at or after t (their keys are unchanged; their own q is)
+        assert torch.equal(res[0][0][:, :, t:], res[1][0][:, :, t:]), "dq"

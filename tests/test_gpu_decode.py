@@ -37,7 +37,7 @@ def run_decode(oracle, torch, B, H, S, D, nq, causal, theta, seed, pos_offset=0,
     torch.cuda.synchronize()
     rows = np.arange(S - nq, S, dtype=np.int64)
     ro, rlse = oracle.attn_fwd(to64(q), to64(k), to64(v), None, pos, theta=theta, causal=causal, rows=rows)
-    eo = assert_parity(to64(o), ro, "O")
+    eo = assert_parity(o, ro, "O")
     el = assert_parity(lse.cpu().numpy(), rlse, "LSE")
     print("  (max, mean) abs errors O %s LSE %s" % (eo, el), flush=True)
     return o, lse
@@ -73,7 +73,7 @@ def test_decode_equals_forward_last_rows(torch_cuda):
     kc = bw.rope_apply(k, None, theta=1e6)
     o_d, lse_d = bw.attn_decode(q[:, :, S - nq:].contiguous(), kc, v, None, theta=1e6)
     torch.cuda.synchronize()
-    assert_parity(to64(o_d), to64(o_f[:, :, S - nq:]), "O decode vs forward", max_abs=1e-2, mean_abs=1e-3)
+    assert_parity(o_d, to64(o_f[:, :, S - nq:]), "O decode vs forward", max_abs=1e-2, mean_abs=1e-3)
     assert_parity(lse_d.cpu().numpy(), lse_f[:, :, S - nq:].cpu().numpy(), "LSE decode vs forward",
                   max_abs=1e-3, mean_abs=1e-4)
 
@@ -102,7 +102,7 @@ def test_decode_full_1m(oracle, torch_cuda):
         qh[0, 0, S - nq:] = to64(q[:, h])[0]
         ro, rlse = oracle.attn_fwd(qh, to64(k[:, h:h + 1]), to64(v[:, h:h + 1]), None, pos, theta=w.theta,
                                    causal=True, rows=rows)
-        eo = assert_parity(to64(o[:, h:h + 1]), ro, "O h%d" % h)
+        eo = assert_parity(o[:, h:h + 1], ro, "O h%d" % h)
         el = assert_parity(lse[:, h:h + 1].cpu().numpy(), rlse, "LSE h%d" % h)
         print("  head %d: (max, mean) abs errors O %s LSE %s" % (h, eo, el), flush=True)
     del q, k, v, o, lse

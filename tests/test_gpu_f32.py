@@ -110,16 +110,6 @@ def test_bwd_f32_matches_oracle(oracle, torch_cuda, B, H, S, D, n_docs, causal, 
     o, lse = bw.attn_fwd_f32(qc, kc, vc, dseg, dpos, theta=theta, causal=causal, kv_chunk=kv_chunk)
     dq, dk, dv = bw.attn_bwd_f32(qc, kc, vc, o, lse, doc, dseg, dpos, theta=theta, causal=causal, kv_chunk=kv_chunk)
     torch.cuda.synchronize()
-    bad = {n: np.argwhere(~np.isfinite(to64(t))) for n, t in (("dq", dq), ("dk", dk), ("dv", dv))}
-    if any(len(b) for b in bad.values()):
-        for n, b in bad.items():
-            print("  %s: %d non-finite, (b, h, row) %s" % (n, len(b), np.unique(b[:, :3], axis=0)[:16].tolist()))
-        again = bw.attn_bwd_f32(qc, kc, vc, o, lse, doc, dseg, dpos, theta=theta, causal=causal, kv_chunk=kv_chunk)
-        torch.cuda.synchronize()
-        print("  second call: non-finite counts %s, equal to the first where finite: %s" % (
-            [int((~torch.isfinite(t)).sum()) for t in again],
-            [bool(torch.equal(torch.nan_to_num(x), torch.nan_to_num(y))) for x, y in zip(again, (dq, dk, dv))]),
-            flush=True)
     rdq, rdk, rdv = oracle.attn_bwd(to64(q), to64(k), to64(v), to64(do), seg, pos, theta=theta, causal=causal)
     check(to64(dq), rdq, "dq")
     check(to64(dk), rdk, "dk")

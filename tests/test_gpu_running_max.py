@@ -10,16 +10,29 @@ increasing order (the decode each chunk so), every row that reaches the
 unbiased keys raises its max once, mid-walk.  The bias is large but its
 keys' probabilities are tiny, so the scores that matter stay of the usual
 size.  Forward and decode (the kernels with a running max) against the
-oracle; the backward recomputes P from the forward's LSE, checked here.
-(Its gradients are not compared on these inputs: a key element of -24
-multiplies the bf16 rounding of dS in dq's bias dimension, where the exact
-sum cancels, and that alone exceeds the absolute bar.)"""
+oracle, and the backward, which recomputes P from the forward's LSE.
+
+The gradients of these inputs carry the rounding of the bf16 MFMA operands
+magnified by the bias: dq_i = scale sum_j dS_ij k'_j takes each dS_ij
+rounded to bf16 (relative error up to 2^-9) times a key element of -24, and
+in the bias dimension the exact sum cancels (rows of dS sum to zero), so the
+rounding alone can exceed the absolute bar.  dS_ij = P_ij (dP_ij - Delta_i)
+also inherits the relative error of P_ij, which the bf16 rounding of the
+rotated rows q'' = q' scale log2(e) and k' puts into the score: at most
+e_ij = 2^-8 scale sum_d |q'_i[d]| |k'_j[d]| (natural-log units; each
+operand rounded once).  Their bar is therefore the absolute one plus the
+bound of these roundings, per element:
+  dq_i[d]: scale sum_j |dS_ij| |k'_j[d]| (2^-8 + e_ij)  (dS, k' rounded once),
+  dk_j[d]: scale sum_i |dS_ij| |q'_i[d]| (2^-8 + e_ij),
+  dv_j[d]: sum_i P_ij |dO_i[d]| (2^-9 + e_ij)           (P rounded once),
+with P, dS, q' and k' from the oracle (attn_probs).  The mean-abs bar stays
+2e-3."""
 import math
 
 import numpy as np
 import pytest
 
-from helpers import assert_parity, to64
+from helpers import MAX_ABS, assert_parity, to64
 
 # the bias sits in the last RoPE pair, which turns by less than 2e-3 rad over
 # these positions at theta 1e6
@@ -53,17 +66,17 @@ def bias_query_value(D):
     return float(cand[i])
 
 
-def rising_case(S, D, seed):
+def rising_case(S, D, seed, with_grad_out=False):
     from long_context_blockwise_attn_amd.inputs import random_case
 
-    (q, k, v, _), _, pos = random_case(1, 2, S, D, seed)
+    (q, k, v, do), _, pos = random_case(1, 2, S, D, seed)
     bd = D - 2
     q[..., bd] = bias_query_value(D)
     q[..., bd + 1] = 0.0
     k[..., bd + 1] = 0.0
     k[..., : S // 3, bd] = -24.0
     k[..., S // 3:, bd] = 0.0
-    return q, k, v, pos
+    return (q, k, v, pos, do) if with_grad_out else (q, k, v, pos)
 
 
 def raises_per_row(q, k, causal):
@@ -104,14 +117,29 @@ def test_fwd_with_raised_max(oracle, torch_cuda, D, theta, causal, kv_chunk):
 
     torch = torch_cuda
     S = 1000
-    q, k, v, pos = rising_case(S, D, seed=5)
+    q, k, v, pos, do = rising_case(S, D, seed=5, with_grad_out=True)
     print("rising keys S%d D%d theta %g causal %d chunk %d" % (S, D, theta, causal, kv_chunk), flush=True)
     dpos = torch.from_numpy(pos).cuda()
-    o, lse = bw.attn_fwd(q.cuda(), k.cuda(), v.cuda(), None, dpos, theta=theta, causal=causal, kv_chunk=kv_chunk)
+    qc, kc, vc, dc = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    o, lse = bw.attn_fwd(qc, kc, vc, None, dpos, theta=theta, causal=causal, kv_chunk=kv_chunk)
+    dq, dk, dv = bw.attn_bwd(qc, kc, vc, o, lse, dc, None, dpos, theta=theta, causal=causal, kv_chunk=kv_chunk)
     torch.cuda.synchronize()
     ro, rlse = oracle.attn_fwd(to64(q), to64(k), to64(v), None, pos, theta=theta, causal=causal)
-    assert_parity(to64(o), ro, "O")
+    assert_parity(o, ro, "O")
     assert_parity(lse.cpu().numpy(), rlse, "LSE")
+    rdq, rdk, rdv = oracle.attn_bwd(to64(q), to64(k), to64(v), to64(do), None, pos, theta=theta, causal=causal)
+    P, dS, qr, kr = oracle.attn_probs(to64(q), to64(k), to64(v), to64(do), None, pos, theta=theta, causal=causal)
+    scale, u = 1.0 / math.sqrt(D), 2.0 ** -8
+    e = u * scale * (np.abs(qr) @ np.swapaxes(np.abs(kr), -1, -2))  # score rounding bound per pair
+    tr = lambda x: np.swapaxes(x, -1, -2)  # noqa: E731
+    bar_dq = MAX_ABS + scale * ((np.abs(dS) * (u + e)) @ np.abs(kr))
+    bar_dk = MAX_ABS + scale * (tr(np.abs(dS) * (u + e)) @ np.abs(qr))
+    bar_dv = MAX_ABS + tr(P * (u / 2 + e)) @ np.abs(to64(do))
+    print("  rounding bound on top of the bar: dq up to %.3g, dk up to %.3g, dv up to %.3g" % (
+        bar_dq.max() - MAX_ABS, bar_dk.max() - MAX_ABS, bar_dv.max() - MAX_ABS), flush=True)
+    assert_parity(dq, rdq, "dq", max_abs=bar_dq)
+    assert_parity(dk, rdk, "dk", max_abs=bar_dk)
+    assert_parity(dv, rdv, "dv", max_abs=bar_dv)
 
 
 @pytest.mark.gpu
@@ -130,5 +158,5 @@ def test_decode_with_raised_max(oracle, torch_cuda, theta):
     torch.cuda.synchronize()
     rows = np.arange(S - nq, S, dtype=np.int64)
     ro, rlse = oracle.attn_fwd(to64(q), to64(k), to64(v), None, pos, theta=theta, causal=True, rows=rows)
-    assert_parity(to64(o), ro, "O")
+    assert_parity(o, ro, "O")
     assert_parity(lse.cpu().numpy(), rlse, "LSE")

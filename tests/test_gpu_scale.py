@@ -46,11 +46,11 @@ def test_fwd_bwd_with_scale(oracle, torch_cuda, path, D, scale, theta, causal):
     ro, rlse = oracle.attn_fwd(to64(q), to64(k), to64(v), seg, pos, theta=theta, scale=scale, causal=causal)
     rdq, rdk, rdv = oracle.attn_bwd(to64(q), to64(k), to64(v), to64(do), seg, pos, theta=theta, scale=scale,
                                     causal=causal)
-    assert_parity(to64(o), ro, "O", **bars)
+    assert_parity(o, ro, "O", **bars)
     assert_parity(lse.cpu().numpy(), rlse, "LSE", **bars)
-    assert_parity(to64(dq), rdq, "dq", **bars)
-    assert_parity(to64(dk), rdk, "dk", **bars)
-    assert_parity(to64(dv), rdv, "dv", **bars)
+    assert_parity(dq, rdq, "dq", **bars)
+    assert_parity(dk, rdk, "dk", **bars)
+    assert_parity(dv, rdv, "dv", **bars)
 
 
 def test_decode_with_scale(oracle, torch_cuda):
@@ -67,5 +67,5 @@ def test_decode_with_scale(oracle, torch_cuda):
     torch.cuda.synchronize()
     rows = np.arange(S - nq, S, dtype=np.int64)
     ro, rlse = oracle.attn_fwd(to64(q), to64(k), to64(v), None, pos, theta=theta, scale=scale, causal=True, rows=rows)
-    assert_parity(to64(o), ro, "O")
+    assert_parity(o, ro, "O")
     assert_parity(lse.cpu().numpy(), rlse, "LSE")

@@ -48,11 +48,11 @@ def test_interleaved_segments(oracle, torch_cuda, path, causal, kv_chunk):
     bars = dict(max_abs=2e-4, mean_abs=2e-5) if f32 else {}
     ro, rlse = oracle.attn_fwd(to64(q), to64(k), to64(v), seg, pos, theta=1e6, causal=causal)
     rdq, rdk, rdv = oracle.attn_bwd(to64(q), to64(k), to64(v), to64(do), seg, pos, theta=1e6, causal=causal)
-    assert_parity(to64(o), ro, "O", **bars)
+    assert_parity(o, ro, "O", **bars)
     assert_parity(lse.cpu().numpy(), rlse, "LSE", **bars)
-    assert_parity(to64(dq), rdq, "dq", **bars)
-    assert_parity(to64(dk), rdk, "dk", **bars)
-    assert_parity(to64(dv), rdv, "dv", **bars)
+    assert_parity(dq, rdq, "dq", **bars)
+    assert_parity(dk, rdk, "dk", **bars)
+    assert_parity(dv, rdv, "dv", **bars)
 
 
 # Two batch rows packed differently: every per-row table (segment block
@@ -85,11 +85,11 @@ def test_batch_rows_with_different_packings(oracle, torch_cuda, path, causal):
     bars = dict(max_abs=2e-4, mean_abs=2e-5) if f32 else {}
     ro, rlse = oracle.attn_fwd(to64(q), to64(k), to64(v), seg, pos, theta=1e6, causal=causal)
     rdq, rdk, rdv = oracle.attn_bwd(to64(q), to64(k), to64(v), to64(do), seg, pos, theta=1e6, causal=causal)
-    assert_parity(to64(o), ro, "O", **bars)
+    assert_parity(o, ro, "O", **bars)
     assert_parity(lse.cpu().numpy(), rlse, "LSE", **bars)
-    assert_parity(to64(dq), rdq, "dq", **bars)
-    assert_parity(to64(dk), rdk, "dk", **bars)
-    assert_parity(to64(dv), rdv, "dv", **bars)
+    assert_parity(dq, rdq, "dq", **bars)
+    assert_parity(dk, rdk, "dk", **bars)
+    assert_parity(dv, rdv, "dv", **bars)
 
 
 # Many documents shorter than a tile: every 32-row block and every tile holds
@@ -120,8 +120,8 @@ def test_many_tiny_documents(oracle, torch_cuda, path, causal, kv_chunk):
     bars = dict(max_abs=2e-4, mean_abs=2e-5) if f32 else {}
     ro, rlse = oracle.attn_fwd(to64(q), to64(k), to64(v), seg, pos, theta=1e6, causal=causal)
     rdq, rdk, rdv = oracle.attn_bwd(to64(q), to64(k), to64(v), to64(do), seg, pos, theta=1e6, causal=causal)
-    assert_parity(to64(o), ro, "O", **bars)
+    assert_parity(o, ro, "O", **bars)
     assert_parity(lse.cpu().numpy(), rlse, "LSE", **bars)
-    assert_parity(to64(dq), rdq, "dq", **bars)
-    assert_parity(to64(dk), rdk, "dk", **bars)
-    assert_parity(to64(dv), rdv, "dv", **bars)
+    assert_parity(dq, rdq, "dq", **bars)
+    assert_parity(dk, rdk, "dk", **bars)
+    assert_parity(dv, rdv, "dv", **bars)
