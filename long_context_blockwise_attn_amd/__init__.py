@@ -122,7 +122,7 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def _check_bhsd(name, t, shape=None, f32=False):
+def _check_bhsd(name, t, shape=None, f32=False, device=None):
     import torch
 
     dt = torch.float32 if f32 else torch.bfloat16
@@ -130,16 +130,44 @@ def _check_bhsd(name, t, shape=None, f32=False):
         raise AttnError("%s must be a contiguous %s CUDA tensor [B,H,S,D]" % (name, "fp32" if f32 else "bf16"))
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise AttnError("%s has shape %r, expected %r" % (name, tuple(t.shape), tuple(shape)))
+    _check_device(name, t, device)
 
 
-def _check_bs(name, t, B, S):
+def _check_device(name, t, device):
+    if device is not None and t.device != device:
+        raise AttnError("%s is on %s, the other tensors on %s" % (name, t.device, device))
+
+
+def _check_bs(name, t, B, S, device=None):
     import torch
 
     if t is None:
         return None
     if t.dtype != torch.int32 or tuple(t.shape) != (B, S) or not t.is_contiguous() or not t.is_cuda:
         raise AttnError("%s must be a contiguous int32 CUDA tensor [B,S]" % name)
+    _check_device(name, t, device)
     return t
+
+
+def _check_lse(lse, shape, device):
+    """lse: a contiguous fp32 CUDA tensor of the given shape on `device`."""
+    import torch
+
+    if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(shape) or not lse.is_contiguous() or not lse.is_cuda:
+        raise AttnError("lse must be a contiguous fp32 CUDA tensor %r" % (list(shape),))
+    _check_device("lse", lse, device)
+
+
+def _check_workspace(workspace, need, device):
+    """A caller-supplied workspace: a contiguous CUDA tensor on `device` of
+    at least `need` bytes.  Returns its size in bytes."""
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise AttnError("workspace must be a contiguous CUDA tensor")
+    _check_device("workspace", workspace, device)
+    nbytes = workspace.numel() * workspace.element_size()
+    if nbytes < need:
+        raise AttnError("workspace of %d bytes needed, %d given" % (need, nbytes))
+    return nbytes
 
 
 def workspace_bytes(params: Params, which: int) -> int:
@@ -155,7 +183,7 @@ def _workspace(params, which, workspace, device):
     need = workspace_bytes(params, which)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=device)
-    return workspace, workspace.numel() * workspace.element_size()
+    return workspace, _check_workspace(workspace, need, device)
 
 
 def _rope(fn, f32, x, positions, theta, inverse, out):
@@ -163,10 +191,11 @@ def _rope(fn, f32, x, positions, theta, inverse, out):
 
     _check_bhsd("x", x, f32=f32)
     B, H, S, D = x.shape
-    _check_bs("positions", positions, B, S)
-    if out is None:
+    _check_bs("positions", positions, B, S, x.device)
+    if out is not None:
+        _check_bhsd("out", out, x.shape, f32=f32, device=x.device)
+    else:
         out = torch.empty_like(x)
-    _check_bhsd("out", out, x.shape, f32=f32)
     p = make_params(B, H, S, D, theta=theta)
     _raise(fn(ctypes.byref(p), _ptr(x), _ptr(out), _ptr(positions), int(bool(inverse)), _stream()))
     return out
@@ -187,15 +216,19 @@ def _fwd(fn, f32, q, k, v, segment_ids, positions, theta, causal, scale, kv_chun
 
     _check_bhsd("q", q, f32=f32)
     B, H, S, D = q.shape
-    _check_bhsd("k", k, q.shape, f32=f32)
-    _check_bhsd("v", v, q.shape, f32=f32)
-    _check_bs("segment_ids", segment_ids, B, S)
-    _check_bs("positions", positions, B, S)
+    dev = q.device
+    _check_bhsd("k", k, q.shape, f32=f32, device=dev)
+    _check_bhsd("v", v, q.shape, f32=f32, device=dev)
+    _check_bs("segment_ids", segment_ids, B, S, dev)
+    _check_bs("positions", positions, B, S, dev)
+    if out is not None:
+        _check_bhsd("out", out, q.shape, f32=f32, device=dev)
+    if lse is not None:
+        _check_lse(lse, (B, H, S), dev)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
-        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
-    _check_bhsd("out", out, q.shape, f32=f32)
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
     p = make_params(B, H, S, D, theta=theta, causal=causal, scale=scale, kv_chunk=kv_chunk)
     ws, nbytes = _workspace(p, 2 if f32 else 0, workspace, q.device)
     _raise(fn(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(segment_ids), _ptr(positions), _ptr(out), _ptr(lse),
@@ -223,17 +256,18 @@ def _bwd(fn, f32, q, k, v, o, lse, dout, segment_ids, positions, theta, causal, 
 
     _check_bhsd("q", q, f32=f32)
     B, H, S, D = q.shape
+    dev = q.device
     for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
-        _check_bhsd(name, t, q.shape, f32=f32)
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, S) or not lse.is_contiguous():
-        raise AttnError("lse must be a contiguous fp32 tensor [B,H,S]")
-    _check_bs("segment_ids", segment_ids, B, S)
-    _check_bs("positions", positions, B, S)
+        _check_bhsd(name, t, q.shape, f32=f32, device=dev)
+    _check_lse(lse, (B, H, S), dev)
+    _check_bs("segment_ids", segment_ids, B, S, dev)
+    _check_bs("positions", positions, B, S, dev)
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t is not None:
+            _check_bhsd(name, t, q.shape, f32=f32, device=dev)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
-    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-        _check_bhsd(name, t, q.shape, f32=f32)
     p = make_params(B, H, S, D, theta=theta, causal=causal, scale=scale, kv_chunk=kv_chunk)
     ws, nbytes = _workspace(p, 3 if f32 else 1, workspace, q.device)
     _raise(fn(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(segment_ids),
@@ -273,21 +307,25 @@ def attn_decode(q, k_cache, v_cache, q_positions=None, theta=0.0, causal=True, s
 
     _check_bhsd("q", q)
     B, H, nq, D = q.shape
-    _check_bhsd("k_cache", k_cache)
+    dev = q.device
+    _check_bhsd("k_cache", k_cache, device=dev)
     S = k_cache.shape[2]
     _check_bhsd("k_cache", k_cache, (B, H, S, D))
-    _check_bhsd("v_cache", v_cache, (B, H, S, D))
-    _check_bs("q_positions", q_positions, B, nq)
+    _check_bhsd("v_cache", v_cache, (B, H, S, D), device=dev)
+    _check_bs("q_positions", q_positions, B, nq, dev)
+    if out is not None:
+        _check_bhsd("out", out, q.shape, device=dev)
+    if lse is not None:
+        _check_lse(lse, (B, H, nq), dev)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
-        lse = torch.empty((B, H, nq), dtype=torch.float32, device=q.device)
-    _check_bhsd("out", out, q.shape)
+        lse = torch.empty((B, H, nq), dtype=torch.float32, device=dev)
     p = make_params(B, H, S, D, theta=theta, causal=causal, scale=scale)
     need = decode_workspace_bytes(p, nq)
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    nbytes = workspace.numel() * workspace.element_size()
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    nbytes = _check_workspace(workspace, need, dev)
     _raise(load().attn_decode(ctypes.byref(p), int(nq), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(q_positions),
                               _ptr(out), _ptr(lse), _ptr(workspace), nbytes, _stream()))
     return out, lse
@@ -312,23 +350,27 @@ def packed_ce_loss(logits, targets, segment_ids=None, num_segments=1, grad_scale
     if logits.dtype != torch.bfloat16 or logits.dim() != 3 or not logits.is_contiguous() or not logits.is_cuda:
         raise AttnError("logits must be a contiguous bf16 CUDA tensor [B,S,V]")
     B, S, V = logits.shape
-    _check_bs("targets", targets, B, S)
+    dev = logits.device
     if targets is None:
         raise AttnError("targets are required")
-    _check_bs("segment_ids", segment_ids, B, S)
+    _check_bs("targets", targets, B, S, dev)
+    _check_bs("segment_ids", segment_ids, B, S, dev)
+    if not with_grad:
+        dlogits = None
+    elif dlogits is not None:
+        if (tuple(dlogits.shape) != tuple(logits.shape) or dlogits.dtype != torch.bfloat16
+                or not dlogits.is_contiguous() or not dlogits.is_cuda):
+            raise AttnError("dlogits must be a contiguous bf16 CUDA tensor shaped like logits")
+        _check_device("dlogits", dlogits, dev)
     p = make_ce_params(B, S, V, num_segments, grad_scale)
     need = packed_ce_workspace_bytes(p)
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
-    loss = torch.empty(1, dtype=torch.float32, device=logits.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    nbytes = _check_workspace(workspace, need, dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
     if with_grad and dlogits is None:
         dlogits = torch.empty_like(logits)
-    if not with_grad:
-        dlogits = None
-    elif dlogits.shape != logits.shape or dlogits.dtype != torch.bfloat16 or not dlogits.is_contiguous():
-        raise AttnError("dlogits must be a contiguous bf16 tensor shaped like logits")
-    tce = torch.empty((B, S), dtype=torch.float32, device=logits.device) if with_token_ce else None
+    tce = torch.empty((B, S), dtype=torch.float32, device=dev) if with_token_ce else None
     _raise(load().packed_ce_loss(ctypes.byref(p), _ptr(logits), _ptr(targets), _ptr(segment_ids), _ptr(loss),
-                                 _ptr(dlogits), _ptr(tce), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                 _stream()))
+                                 _ptr(dlogits), _ptr(tce), _ptr(workspace), nbytes, _stream()))
     return loss, dlogits, tce

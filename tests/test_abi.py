@@ -215,3 +215,93 @@ def test_packed_ce_argument_errors_before_any_hip_call(lib):
     assert n == 256 + 256 + 1024 * 4  # counts, weights (64 each, 256-byte aligned), one float per row
     assert call(ws=4096, nbytes=n - 1) == 3
     assert lib.packed_ce_workspace_bytes(ctypes.byref(bw.make_ce_params(1, 8, 7))) == 0
+
+
+class FakeTensor:
+    """Stands in for a torch tensor in the binding's argument checks (no
+    device memory is touched: every case below is refused before the
+    library is called)."""
+
+    def __init__(self, shape, dtype, device="cuda:0", contiguous=True):
+        import torch
+
+        self.shape = tuple(shape)
+        self.dtype = dtype
+        self.device = torch.device(device)
+        self.is_cuda = self.device.type == "cuda"
+        self._contiguous = contiguous
+
+    def dim(self):
+        return len(self.shape)
+
+    def is_contiguous(self):
+        return self._contiguous
+
+    def numel(self):
+        n = 1
+        for s in self.shape:
+            n *= s
+        return n
+
+    def element_size(self):
+        import torch
+
+        return {torch.bfloat16: 2, torch.float32: 4, torch.int32: 4, torch.uint8: 1}[self.dtype]
+
+    def data_ptr(self):
+        raise AssertionError("the binding passed a refused tensor to the library")
+
+
+def test_binding_refuses_bad_lse_and_workspace():
+    """lse and the workspace are checked for dtype, shape, contiguity and
+    device before any pointer reaches the library (a host pointer or a short
+    buffer would otherwise be handed to the kernels)."""
+    import torch
+
+    import long_context_blockwise_attn_amd as bw
+
+    B, H, S, D = 1, 2, 64, 128
+    bf = torch.bfloat16
+
+    def t(shape=(B, H, S, D), dtype=bf, device="cuda:0", contiguous=True):
+        return FakeTensor(shape, dtype, device, contiguous)
+
+    q, k, v, o, do = t(), t(), t(), t(), t()
+    good_lse = t((B, H, S), torch.float32)
+    bad_lses = [t((B, H, S), torch.float32, device="cpu"), t((B, H, S - 1), torch.float32),
+                t((B, H, S), bf), t((B, H, S), torch.float32, contiguous=False),
+                t((B, H, S), torch.float32, device="cuda:1")]
+    for lse in bad_lses:
+        with pytest.raises(bw.AttnError, match="lse"):
+            bw.attn_fwd(q, k, v, lse=lse, out=o)
+        with pytest.raises(bw.AttnError, match="lse"):
+            bw.attn_bwd(q, k, v, o, lse, do, dq=t(), dk=t(), dv=t())
+    for ws in [t((1 << 20,), torch.uint8, device="cpu"), t((1 << 20,), torch.uint8, device="cuda:1"),
+               t((16,), torch.uint8)]:
+        with pytest.raises(bw.AttnError, match="workspace"):
+            bw.attn_fwd(q, k, v, lse=good_lse, out=o, workspace=ws)
+        with pytest.raises(bw.AttnError, match="workspace"):
+            bw.attn_bwd(q, k, v, o, good_lse, do, dq=t(), dk=t(), dv=t(), workspace=ws)
+    # every tensor on q's device
+    with pytest.raises(bw.AttnError, match="k is on"):
+        bw.attn_fwd(q, t(device="cuda:1"), v, lse=good_lse, out=o)
+    with pytest.raises(bw.AttnError, match="dv is on"):
+        bw.attn_bwd(q, k, v, o, good_lse, do, dq=t(), dk=t(), dv=t(device="cuda:1"))
+    with pytest.raises(bw.AttnError, match="segment_ids is on"):
+        bw.attn_fwd(q, k, v, FakeTensor((B, S), torch.int32, "cuda:1"), lse=good_lse, out=o)
+    with pytest.raises(bw.AttnError, match="segment_ids"):
+        bw.attn_fwd(q, k, v, FakeTensor((B, S), torch.int32, "cpu"), lse=good_lse, out=o)
+    # decode: lse, out and workspace alike
+    qd = t((B, H, 4, D))
+    with pytest.raises(bw.AttnError, match="lse"):
+        bw.attn_decode(qd, k, v, out=t((B, H, 4, D)), lse=t((B, H, 4), torch.float32, device="cpu"))
+    with pytest.raises(bw.AttnError, match="workspace"):
+        bw.attn_decode(qd, k, v, out=t((B, H, 4, D)), lse=t((B, H, 4), torch.float32),
+                       workspace=t((1 << 20,), torch.uint8, device="cpu"))
+    # packed cross-entropy: dlogits and workspace
+    logits = t((B, S, 64))
+    tg = FakeTensor((B, S), torch.int32)
+    with pytest.raises(bw.AttnError, match="dlogits"):
+        bw.packed_ce_loss(logits, tg, dlogits=t((B, S, 64), device="cpu"))
+    with pytest.raises(bw.AttnError, match="workspace"):
+        bw.packed_ce_loss(logits, tg, dlogits=t((B, S, 64)), workspace=t((8,), torch.uint8))
