@@ -158,8 +158,17 @@ struct CeArgs {
   int B, S, V, num_segments;
   float grad_scale;
 };
+constexpr int kCeThreads = 512;     // threads per row workgroup (8 waves)
 constexpr int kCeMaxVocab = 65536;  // 512 threads x 16 chunks x 8 logits held in registers
-int ce_chunks_per_thread(int V);  // 16-byte chunks per thread of the row kernel, -1 if V is too large
+// 16-byte chunks per thread of the row kernel (one of its compiled sizes),
+// -1 if V is too large
+inline int ce_chunks_per_thread(int V) {
+  const int need = ((V >> 3) + kCeThreads - 1) / kCeThreads;
+  const int opts[] = {2, 4, 6, 8, 10, 12, 16};
+  for (int o : opts)
+    if (need <= o) return o;
+  return -1;
+}
 
 hipError_t launch_packed_ce_prologue(const CeArgs& a, hipStream_t st);
 hipError_t launch_packed_ce_rows(const CeArgs& a, hipStream_t st);

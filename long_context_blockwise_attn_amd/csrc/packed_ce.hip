@@ -25,8 +25,6 @@ namespace bwattn {
 
 namespace {
 
-constexpr int kCeThreads = 512;  // threads per row workgroup (8 waves)
-
 __device__ __forceinline__ bool ce_loss_row(const CeArgs& a, int64_t t, int& key) {
   const int y = a.targets[t];
   const int b = (int)(t / a.S);
@@ -205,14 +203,6 @@ __global__ __launch_bounds__(1024) void ce_sum_kernel(CeArgs a) {
     for (int i = 0; i < (int)(blockDim.x >> 6); ++i) tot += part[i];
     *a.loss = (float)tot;
   }
-}
-
-int ce_chunks_per_thread(int V) {
-  const int need = ((V >> 3) + kCeThreads - 1) / kCeThreads;
-  const int opts[] = {2, 4, 6, 8, 10, 12, 16};
-  for (int o : opts)
-    if (need <= o) return o;
-  return -1;
 }
 
 hipError_t launch_packed_ce_prologue(const CeArgs& a, hipStream_t st) {
