@@ -80,10 +80,13 @@ def cpu_baseline(w, q, k, v, do, seg, pos, budget_s):
     while dt < 0.5 * budget_s and n < S:
         n = int(min(S, max(2 * n, n * 0.75 * budget_s / max(dt, 1e-3))))
         rows, dt, flops = run(n)
+    model, avail = host_cpu()
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": oracle.num_threads(),
+        "cpu_model": model,
+        "host_cores_available": avail,
         "kind": "oracle",
         "sample": "fwd+bwd of %d evenly spaced query rows of head 0 (of %d rows x %d heads), %.1f s; "
                   "credited 14*D FLOPs per visible pair of those rows" % (len(rows), S, w.heads, dt),
@@ -172,6 +175,105 @@ def load_traffic(workload, kernel):
         return None
     k = rec.get("kernels", {}).get(kernel)
     return None if k is None else k.get("traffic_bytes")
+
+
+def counters_path(workload):
+    return os.path.join(ROOT, "profiles", "counters_%s.json" % workload)
+
+
+# MFMA instruction counters: the hardware counts matrix work in units of 512
+# FLOPs ("MOPS"); one counter per data type
+MOPS_COUNTER = {"bf16": "SQ_INSTS_VALU_MFMA_MOPS_BF16", "f32": "SQ_INSTS_VALU_MFMA_MOPS_F32"}
+
+
+def write_counter_record(workload, csvs, command, simds=1024, xcds=8):
+    """Per-dispatch averages of every counter in the rocprofv3 --pmc CSVs
+    (one pass each) for the timed kernels, with the kernel sources' hash, the
+    dispatches' own durations (from the CSV timestamps) and what follows from
+    them:
+      - GRBM_GUI_ACTIVE counts the busy cycles of each of the `xcds`
+        dies, so GRBM_GUI_ACTIVE / xcds / duration is the clock the kernel
+        ran at;
+      - SQ_VALU_MFMA_BUSY_CYCLES sums the matrix units' busy cycles over the
+        `simds` SIMDs, so its share of simds x those cycles is the MFMA
+        utilisation at that clock;
+      - SQ_INSTS_VALU_MFMA_MOPS_BF16 (_F32) counts MFMA work in units of 512
+        FLOPs."""
+    import csv
+
+    rec = {"workload": workload, "source_sha256": kernel_source_hash(), "command": command, "simds": simds,
+           "xcds": xcds, "kernels": {}}
+    for path in csvs:
+        rows, durs = {}, {}
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                rows.setdefault((r["Kernel_Name"], r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+                durs.setdefault(r["Kernel_Name"], {})[r["Dispatch_Id"]] = (
+                    int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+        for (kname, counter), vals in rows.items():
+            for name, sym in KERNEL_SYMBOLS.items():
+                if sym in kname:
+                    k = rec["kernels"].setdefault(name, {})
+                    k[counter] = float(np.mean(vals))
+                    k.setdefault("dispatches", {})[counter] = len(vals)
+                    k.setdefault("pmc_run_ms", {})[os.path.basename(path)] = 1e3 * float(
+                        np.mean(list(durs[kname].values())))
+    for k in rec["kernels"].values():
+        ms = float(np.mean(list(k["pmc_run_ms"].values())))
+        if "GRBM_GUI_ACTIVE" in k:
+            cycles = k["GRBM_GUI_ACTIVE"] / xcds
+            k["clock_ghz"] = cycles / (ms * 1e-3) / 1e9
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in k:
+                k["mfma_util_at_clock"] = k["SQ_VALU_MFMA_BUSY_CYCLES"] / (simds * cycles)
+    with open(counters_path(workload), "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
+def load_counters(workload, kernel, avg_ms, peak):
+    """Matrix-unit figures of `kernel` from the stored counter record (None
+    when there is none or the kernels changed since it was taken): the MFMA
+    FLOPs the hardware counted per launch and their rate over the live
+    average launch time, against the dtype's peak; the clock the kernel ran
+    at in the counter run and the MFMA utilisation at that clock; the raw
+    counters per launch (VALU activity, LDS bank conflicts)."""
+    try:
+        with open(counters_path(workload)) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    if not k:
+        return None
+    dtype = "f32" if kernel.endswith("_f32") else "bf16"
+    out = {"source": os.path.relpath(counters_path(workload), ROOT)}
+    mops = k.get(MOPS_COUNTER[dtype])
+    if mops is not None:
+        flops = 512.0 * mops
+        out["mfma_flops_per_launch"] = flops
+        out["mfma_tflops"] = flops / (avg_ms * 1e-3) / 1e12
+        out["mfma_frac"] = out["mfma_tflops"] / peak
+    for c in ("clock_ghz", "mfma_util_at_clock", "GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES",
+              "SQ_ACTIVE_INST_VALU", "SQ_LDS_BANK_CONFLICT"):
+        if c in k:
+            out[c] = k[c]
+    return out
+
+
+def host_cpu():
+    """CPU model of this host and the number of cores this process may use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, len(os.sched_getaffinity(0))
 
 
 def event_arrays(lib, torch, names, n_each):
@@ -269,8 +371,9 @@ def decode_bench(args, w):
             reps += 1
             dt = time.perf_counter() - t_start
         head_bytes = 2.0 * S * D * 2 + 2.0 * nq * D * 2 + nq * 4
+        model, avail = host_cpu()
         cpu = {"value": reps * head_bytes / dt / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
-               "kind": "oracle",
+               "cpu_model": model, "host_cores_available": avail, "kind": "oracle",
                "sample": "%d oracle calls on head 0 of %d (the n_q rows against its whole cache, K rotated inside), "
                          "%.1f s; credited that head's bf16 cache bytes per call" % (reps, H, dt),
                "seconds": dt}
@@ -372,7 +475,9 @@ def packed_ce_bench(args, w):
             n = min(S, 2 * n)
         nl = int(((tg[:n] >= 0) & (tg[:n] < V)).sum())
         sample_bytes = 2.0 * nl * V + 2.0 * n * V + 8.0 * n
-        cpu = {"value": sample_bytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+        model, avail = host_cpu()
+        cpu = {"value": sample_bytes / dt / 1e9, "unit": "GB/s", "cores": 1, "cpu_model": model,
+               "host_cores_available": avail, "kind": "oracle",
                "sample": "the first %d rows (%d loss rows) of the packed row, loss and full gradient, %.1f s; "
                          "credited the same bytes per row as the GPU" % (n, nl, dt),
                "seconds": dt}
@@ -406,9 +511,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="llama7b_32k",
-                    help="llama7b_32k (default), packing_128k, video_text_256k, full_1m, tiny, "
-                         "decode_1m (attn_decode; HBM GB/s), packed_ce_32k (packed_ce_loss; HBM GB/s)")
+    ap.add_argument("--workload", default="packing_128k",
+                    help="packing_128k (default: 128K of packed documents, causal + segment mask), llama7b_32k, "
+                         "video_text_256k, full_1m, tiny, decode_1m (attn_decode; HBM GB/s), packed_ce_32k "
+                         "(packed_ce_loss; HBM GB/s)")
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "f32"],
                     help="bf16 (default: attn_fwd/attn_bwd) or f32 (attn_fwd_f32/attn_bwd_f32 on fp32 tensors)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -419,7 +525,15 @@ def main():
                     help="write the HBM traffic record of --workload from two rocprofv3 --pmc counter CSVs "
                          "(FETCH_SIZE, WRITE_SIZE) of runs made with --copy-calibration-mib, then exit")
     ap.add_argument("--traffic-command", default="", help="command line recorded with --traffic-from")
+    ap.add_argument("--counters-from", nargs="+", metavar="PMC_CSV",
+                    help="write the counter record of --workload (profiles/counters_<workload>.json) from rocprofv3 "
+                         "--pmc counter CSVs, then exit")
     args = ap.parse_args()
+
+    if args.counters_from:
+        write_counter_record(args.workload + ("_f32" if args.dtype == "f32" else ""), args.counters_from,
+                             args.traffic_command)
+        return
 
     if args.traffic_from:
         # one record per workload and dtype (profiles/traffic_<workload>[_f32].json)
@@ -481,9 +595,15 @@ def main():
     # live per-kernel timing: HIP events recorded by the library around each
     # launch, on the launch stream, over the timed region
     lib = bw.load()
-    launches = {"rope": 4 if do_bwd else 2, "fwd": 1, "bwd_dq": 1 if do_bwd else 0, "bwd_dkdv": 1 if do_bwd else 0}
-    if w.theta <= 0:
-        launches["rope"] = 0
+    # RoPE pre-pass launches per step: the bf16 forward rotates k (its query
+    # rows are rotated in the kernel's load), the bf16 backward writes q''
+    # (rotated and scaled, also without RoPE) and k'; the fp32 path rotates q
+    # and k in both passes, and nothing without RoPE
+    if f32:
+        rope_launches = (4 if do_bwd else 2) if w.theta > 0 else 0
+    else:
+        rope_launches = (1 if w.theta > 0 else 0) + ((2 if w.theta > 0 else 1) if do_bwd else 0)
+    launches = {"rope": rope_launches, "fwd": 1, "bwd_dq": 1 if do_bwd else 0, "bwd_dkdv": 1 if do_bwd else 0}
     ev = {}
     keep = []
     for name, per in launches.items():
@@ -525,18 +645,31 @@ def main():
     bwd_flops = 10.0 * D * H * pairs if do_bwd else 0.0
     tflops = (fwd_flops + bwd_flops) / (ms_step * 1e-3) / 1e12
 
-    # dominant kernel and its roofline (MFMA bound): contractions it performs,
-    # 2*D FLOPs per visible pair each (fwd 2: QK^T, PV; dQ 3: QK^T, dP, dQ;
-    # dK/dV 4: QK^T, dP, dV, dK)
-    contractions = {"fwd": 2, "bwd_dq": 3, "bwd_dkdv": 4}
-    dom = max((n for n in contractions if n in kernel_ms),
-              key=lambda n: kernel_ms[n]["avg_ms"] * kernel_ms[n]["launches_per_step"])
-    dom_flops = contractions[dom] * 2.0 * D * H * pairs
-    dom_tflops = dom_flops / (kernel_ms[dom]["avg_ms"] * 1e-3) / 1e12
+    # dominant kernel and its roofline (MFMA bound).  Each kernel is credited
+    # the method's contractions it performs, 2*D FLOPs per visible pair each:
+    # fwd 2 (QK^T, PV), dK/dV 4 (QK^T recomputed, dP, dV, dK), dQ 1 (dQ); the
+    # dQ kernel also executes QK^T and dP again (3 in all), which the method's
+    # 10*D backward does not count, so its executed fraction is given apart
+    credited = {"fwd": 2, "bwd_dq": 1, "bwd_dkdv": 4}
+    executed = {"fwd": 2, "bwd_dq": 3, "bwd_dkdv": 4}
     peak = FP32_PEAK_TFLOPS if f32 else BF16_PEAK_TFLOPS
+    per_kernel = {}
+    for n in credited:
+        if n in kernel_ms:
+            t = kernel_ms[n]["avg_ms"] * 1e-3
+            per_kernel[n] = {"ms": round(kernel_ms[n]["avg_ms"], 4),
+                             "frac": credited[n] * 2.0 * D * H * pairs / t / 1e12 / peak,
+                             "executed_frac": executed[n] * 2.0 * D * H * pairs / t / 1e12 / peak}
+    dom = max((n for n in credited if n in kernel_ms),
+              key=lambda n: kernel_ms[n]["avg_ms"] * kernel_ms[n]["launches_per_step"])
+    dom_flops = credited[dom] * 2.0 * D * H * pairs
+    dom_tflops = dom_flops / (kernel_ms[dom]["avg_ms"] * 1e-3) / 1e12
     roofline = {"kernel": dom + sfx, "bound": "mfma", "achieved": dom_tflops, "peak": peak, "unit": "TFLOP/s",
                 "frac": dom_tflops / peak, "traffic": load_traffic(w.name + sfx, dom + sfx),
-                "traffic_unit": "HBM bytes per launch", "flops_per_launch": dom_flops}
+                "traffic_unit": "HBM bytes per launch", "flops_per_launch": dom_flops,
+                "executed_flops_per_launch": executed[dom] * 2.0 * D * H * pairs,
+                "counters": load_counters(w.name + sfx, dom + sfx, kernel_ms[dom]["avg_ms"], peak),
+                "kernels": per_kernel}
 
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20
