@@ -29,8 +29,9 @@
  *     no pointer after returning.  The caller owns every buffer, including the
  *     workspace sized by attn_workspace_bytes, and keeps them alive until the
  *     stream work has finished.  Entry points keep no state (apart from the
- *     thread-local measurement request of attn_profile_events) and are
- *     thread-safe.
+ *     thread-local measurement request of attn_profile_events, and the static
+ *     workspace of attn_decode_noalloc, below) and are thread-safe (calls of
+ *     attn_decode_noalloc that overlap on one GPU excepted).
  *   - Every argument is checked before any HIP call.  The return value is an
  *     attn_status; no exception crosses the ABI and the library never aborts.
  *     Device-side values (segment ids, positions) are not checked: any int32
@@ -74,8 +75,8 @@ typedef struct {
                          /* queries of chunk r visit chunk r, r-1, ..., 0, C-1, ..., r+1.    */
                          /* (attn_bwd walks tiles of 128 rows or keys: its chunks are        */
                          /* rounded down to whole tiles; the result is the same sum.)        */
-  int32_t deterministic; /* reserved, must be 0 or 1; 1 asks attn_bwd for a bitwise          */
-                         /* reproducible result (no float atomics)                           */
+  int32_t deterministic; /* must be 0 or 1.  attn_bwd is bitwise reproducible either way:    */
+                         /* no path uses float atomics, so both values run the same kernels  */
 } attn_params;
 
 /* Name of a status code (static string). */
@@ -173,6 +174,28 @@ int attn_decode(const attn_params* p, int32_t n_q, const void* q, const void* k_
 /* Bytes of device workspace attn_decode needs for these parameters and n_q;
  * 0 if they are invalid. */
 size_t attn_decode_workspace_bytes(const attn_params* p, int32_t n_q);
+
+/* attn_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, token-by-token serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments and results as attn_decode (the same kernels,
+ * so the same bits), minus the workspace: the call uses a static device
+ * array of attn_decode_noalloc_max_bytes() bytes (64 MiB) that the library
+ * holds on every GPU it runs on until the process ends.  It allocates and
+ * frees nothing.
+ *   - Parameters whose attn_decode_workspace_bytes(p, n_q) exceeds that size
+ *     are refused with ATTN_ERR_WORKSPACE before any HIP call (at n_q = 32
+ *     and D = 128 every batch x heads up to 2048 fits).
+ *   - Every call on one GPU shares that GPU's array: calls that overlap in
+ *     time on one GPU (other streams, other host threads) race and give
+ *     wrong results; calls ordered on one stream do not.  Nothing in the
+ *     array needs to start at zero: a call writes every byte it reads.
+ *   - The array's device address is looked up once per device, on the
+ *     first call with that device current. */
+int attn_decode_noalloc(const attn_params* p, int32_t n_q, const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* q_positions, void* o, float* lse, void* stream);
+
+/* Size in bytes of the static workspace of attn_decode_noalloc. */
+size_t attn_decode_noalloc_max_bytes(void);
 
 /* ------------------------------------------------------------------------ */
 /* Loss side of masked sequence packing.  Short examples packed into one row  */

@@ -11,7 +11,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["attn_fwd", "attn_bwd", "attn_decode", "rope_apply", "attn_fwd_f32", "attn_bwd_f32", "rope_apply_f32",
+__all__ = ["attn_fwd", "attn_bwd", "attn_decode", "attn_decode_noalloc", "rope_apply", "attn_fwd_f32", "attn_bwd_f32", "rope_apply_f32",
            "packed_ce_loss", "workspace_bytes", "decode_workspace_bytes", "packed_ce_workspace_bytes", "AttnError",
            "library_path", "Params", "CeParams"]
 
@@ -93,6 +93,10 @@ def load():
         lib.attn_decode.argtypes = [P, ctypes.c_int32, V, V, V, V, V, V, V, ctypes.c_size_t, V]
         lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
         lib.attn_decode_workspace_bytes.argtypes = [P, ctypes.c_int32]
+        lib.attn_decode_noalloc.restype = ctypes.c_int
+        lib.attn_decode_noalloc.argtypes = [P, ctypes.c_int32, V, V, V, V, V, V, V]
+        lib.attn_decode_noalloc_max_bytes.restype = ctypes.c_size_t
+        lib.attn_decode_noalloc_max_bytes.argtypes = []
         CP = ctypes.POINTER(CeParams)
         lib.packed_ce_workspace_bytes.restype = ctypes.c_size_t
         lib.packed_ce_workspace_bytes.argtypes = [CP]
@@ -328,6 +332,36 @@ def attn_decode(q, k_cache, v_cache, q_positions=None, theta=0.0, causal=True, s
     nbytes = _check_workspace(workspace, need, dev)
     _raise(load().attn_decode(ctypes.byref(p), int(nq), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(q_positions),
                               _ptr(out), _ptr(lse), _ptr(workspace), nbytes, _stream()))
+    return out, lse
+
+
+def attn_decode_noalloc(q, k_cache, v_cache, q_positions=None, theta=0.0, causal=True, scale=0.0, out=None,
+                        lse=None):
+    """attn_decode through the entry point that allocates nothing: the
+    library's static device workspace stands in for the caller's (calls that
+    overlap in time on one GPU race).  out and lse, when given, are written
+    in place, so a caller that must not allocate passes both."""
+    import torch
+
+    _check_bhsd("q", q)
+    B, H, nq, D = q.shape
+    dev = q.device
+    _check_bhsd("k_cache", k_cache, device=dev)
+    S = k_cache.shape[2]
+    _check_bhsd("k_cache", k_cache, (B, H, S, D))
+    _check_bhsd("v_cache", v_cache, (B, H, S, D), device=dev)
+    _check_bs("q_positions", q_positions, B, nq, dev)
+    if out is not None:
+        _check_bhsd("out", out, q.shape, device=dev)
+    if lse is not None:
+        _check_lse(lse, (B, H, nq), dev)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, nq), dtype=torch.float32, device=dev)
+    p = make_params(B, H, S, D, theta=theta, causal=causal, scale=scale)
+    _raise(load().attn_decode_noalloc(ctypes.byref(p), int(nq), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                      _ptr(q_positions), _ptr(out), _ptr(lse), _stream()))
     return out, lse
 
 

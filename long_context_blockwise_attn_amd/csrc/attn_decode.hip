@@ -16,6 +16,8 @@
 //  - writes the V rows (read as contiguous 1 KB lines) to its own LDS tile
 //    and takes the V^T operand of O^T += V^T P^T with transposing LDS reads
 //    (ds_read_b64_tr_b16), so the cache needs no transposed copy.
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "tile.hpp"
@@ -220,6 +222,32 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(DecodeArgs a) {
     dst[t + 64 * i] = __builtin_bit_cast(uint32_t, h) & 0xffffu;
   }
   if (t == 0) a.lse[bh * a.n_q + row] = l > 0.f ? (M + __log2f(l)) * kLn2 : kNegInf;
+}
+
+// Workspace of attn_decode_noalloc: a file-scope array in device memory, so
+// that entry point allocates nothing.  Host code never uses the array's name
+// as an address (on the host it only names the symbol): decode_scratch looks
+// up its device address once per device with that device current, and the
+// kernels receive that address.
+static __device__ __align__(256) char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_attn_decode_partial(const DecodeArgs& a, int D, hipStream_t st) {

@@ -342,6 +342,71 @@ int check_decode_rows(int32_t n_q, int S) {
   return ATTN_OK;
 }
 
+// Argument checks of the decode entry points (the workspace aside).
+int check_decode_args(const attn_params* p, int32_t n_q, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* q_positions, const void* o, const float* lse) {
+  int rc = check_params(p);
+  if (rc) return rc;
+  rc = check_decode_rows(n_q, p->seqlen);
+  if (rc) return rc;
+  if (!q || !k_cache || !v_cache || !o || !lse)
+    return fail(ATTN_ERR_INVALID_ARG, "q, k_cache, v_cache, o and lse must not be NULL");
+  const void* ptrs[] = {q, k_cache, v_cache, q_positions, o, lse};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return fail(ATTN_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  return ATTN_OK;
+}
+
+// The decode launch sequence on a workspace laid out by `dp`: every byte the
+// merge reads is written earlier in the same sequence (the query rows by the
+// RoPE pre-pass, the state of every chunk and row by the partial kernel), so
+// the workspace needs no clearing.
+int run_decode(const attn_params* p, const DecodePlan& dp, int32_t n_q, const void* q, const void* k_cache,
+               const void* v_cache, const int32_t* q_positions, void* o, float* lse, char* ws, hipStream_t st) {
+  {
+    // query rows times scale * log2(e), as the forward takes them
+    RopeArgs r{};
+    r.x = (const uint16_t*)q;
+    r.y = (uint16_t*)(ws + dp.off_qr);
+    r.pos = q_positions;
+    r.pos_base = p->seqlen - n_q;
+    r.B = p->batch;
+    r.H = p->heads;
+    r.S = n_q;
+    r.D = p->head_dim;
+    r.inverse = 0;
+    r.out_scale = scale_log2_of(p);
+    if (p->rope_theta > 0.0) fill_turns(r.turns, p->head_dim, p->rope_theta);  // else the identity rotation
+    int rc = hip_status(timed_launch(ATTN_KERNEL_ROPE, st, [&] { return launch_rope(r, st); }), "rope(q) launch");
+    if (rc) return rc;
+  }
+  DecodeArgs a{};
+  a.q = (const uint16_t*)(ws + dp.off_qr);
+  a.k = (const uint16_t*)k_cache;
+  a.v = (const uint16_t*)v_cache;
+  a.part_o = (float*)(ws + dp.off_po);
+  a.part_ml = (float*)(ws + dp.off_ml);
+  a.o = (uint16_t*)o;
+  a.lse = lse;
+  a.B = p->batch;
+  a.H = p->heads;
+  a.S = p->seqlen;
+  a.n_q = n_q;
+  a.n_chunks = dp.n_chunks;
+  a.chunk = dp.chunk;
+  a.causal = p->causal;
+  int rc = hip_status(
+      timed_launch(ATTN_KERNEL_DECODE, st, [&] { return launch_attn_decode_partial(a, p->head_dim, st); }),
+      "attn_decode partial launch");
+  if (rc) return rc;
+  rc = hip_status(
+      timed_launch(ATTN_KERNEL_DECODE_MERGE, st, [&] { return launch_attn_decode_combine(a, p->head_dim, st); }),
+      "attn_decode merge launch");
+  if (rc) return rc;
+  g_err[0] = 0;
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -617,65 +682,36 @@ size_t attn_decode_workspace_bytes(const attn_params* p, int32_t n_q) {
 int attn_decode(const attn_params* p, int32_t n_q, const void* q, const void* k_cache, const void* v_cache,
                 const int32_t* q_positions, void* o, float* lse, void* workspace, size_t workspace_bytes,
                 void* stream) {
-  int rc = check_params(p);
+  int rc = check_decode_args(p, n_q, q, k_cache, v_cache, q_positions, o, lse);
   if (rc) return rc;
-  rc = check_decode_rows(n_q, p->seqlen);
-  if (rc) return rc;
-  if (!q || !k_cache || !v_cache || !o || !lse)
-    return fail(ATTN_ERR_INVALID_ARG, "q, k_cache, v_cache, o and lse must not be NULL");
-  const void* ptrs[] = {q, k_cache, v_cache, q_positions, o, lse, workspace};
-  for (const void* ptr : ptrs)
-    if (!aligned16(ptr)) return fail(ATTN_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  if (!aligned16(workspace)) return fail(ATTN_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
   DecodePlan dp = make_decode_plan(p, n_q);
   if (workspace == nullptr || workspace_bytes < dp.total)
     return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", dp.total, workspace_bytes,
                 workspace ? "" : " (NULL)");
   rc = check_device();
   if (rc) return rc;
-  hipStream_t st = (hipStream_t)stream;
-  char* ws = (char*)workspace;
-  {
-    // query rows times scale * log2(e), as the forward takes them
-    RopeArgs r{};
-    r.x = (const uint16_t*)q;
-    r.y = (uint16_t*)(ws + dp.off_qr);
-    r.pos = q_positions;
-    r.pos_base = p->seqlen - n_q;
-    r.B = p->batch;
-    r.H = p->heads;
-    r.S = n_q;
-    r.D = p->head_dim;
-    r.inverse = 0;
-    r.out_scale = scale_log2_of(p);
-    if (p->rope_theta > 0.0) fill_turns(r.turns, p->head_dim, p->rope_theta);  // else the identity rotation
-    rc = hip_status(timed_launch(ATTN_KERNEL_ROPE, st, [&] { return launch_rope(r, st); }), "rope(q) launch");
-    if (rc) return rc;
-  }
-  DecodeArgs a{};
-  a.q = (const uint16_t*)(ws + dp.off_qr);
-  a.k = (const uint16_t*)k_cache;
-  a.v = (const uint16_t*)v_cache;
-  a.part_o = (float*)(ws + dp.off_po);
-  a.part_ml = (float*)(ws + dp.off_ml);
-  a.o = (uint16_t*)o;
-  a.lse = lse;
-  a.B = p->batch;
-  a.H = p->heads;
-  a.S = p->seqlen;
-  a.n_q = n_q;
-  a.n_chunks = dp.n_chunks;
-  a.chunk = dp.chunk;
-  a.causal = p->causal;
-  rc = hip_status(timed_launch(ATTN_KERNEL_DECODE, st, [&] { return launch_attn_decode_partial(a, p->head_dim, st); }),
-                  "attn_decode partial launch");
-  if (rc) return rc;
-  rc = hip_status(
-      timed_launch(ATTN_KERNEL_DECODE_MERGE, st, [&] { return launch_attn_decode_combine(a, p->head_dim, st); }),
-      "attn_decode merge launch");
-  if (rc) return rc;
-  g_err[0] = 0;
-  return ATTN_OK;
+  return run_decode(p, dp, n_q, q, k_cache, v_cache, q_positions, o, lse, (char*)workspace, (hipStream_t)stream);
 }
+
+int attn_decode_noalloc(const attn_params* p, int32_t n_q, const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* q_positions, void* o, float* lse, void* stream) {
+  int rc = check_decode_args(p, n_q, q, k_cache, v_cache, q_positions, o, lse);
+  if (rc) return rc;
+  DecodePlan dp = make_decode_plan(p, n_q);
+  if (dp.total > kDecodeScratchBytes)
+    return fail(ATTN_ERR_WORKSPACE,
+                "attn_decode_noalloc: these parameters need %zu bytes of workspace, above its static %zu bytes; "
+                "use attn_decode with a workspace", dp.total, kDecodeScratchBytes);
+  rc = check_device();
+  if (rc) return rc;
+  void* ws = nullptr;
+  rc = hip_status(decode_scratch(&ws), "attn_decode_noalloc scratch lookup");
+  if (rc) return rc;
+  return run_decode(p, dp, n_q, q, k_cache, v_cache, q_positions, o, lse, (char*)ws, (hipStream_t)stream);
+}
+
+size_t attn_decode_noalloc_max_bytes(void) { return kDecodeScratchBytes; }
 
 size_t packed_ce_workspace_bytes(const packed_ce_params* p) {
   if (check_ce_params(p) != ATTN_OK) return 0;

@@ -186,4 +186,11 @@ hipError_t launch_attn_bwd_dkdv(const BwdArgs& a, int D, hipStream_t st);
 hipError_t launch_attn_decode_partial(const DecodeArgs& a, int D, hipStream_t st);
 hipError_t launch_attn_decode_combine(const DecodeArgs& a, int D, hipStream_t st);
 
+// Bytes of the file-scope device array that attn_decode_noalloc uses as its
+// workspace (one copy per GPU, alive until the process ends).
+constexpr size_t kDecodeScratchBytes = size_t(64) << 20;
+// Device address of that array on the current device, looked up once per
+// device (hipGetSymbolAddress) and cached.
+hipError_t decode_scratch(void** ptr);
+
 }  // namespace bwattn

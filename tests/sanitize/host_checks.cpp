@@ -37,6 +37,7 @@ STAND_IN(hipError_t launch_attn_bwd_dq(const BwdArgs&, int, hipStream_t))
 STAND_IN(hipError_t launch_attn_bwd_dkdv(const BwdArgs&, int, hipStream_t))
 STAND_IN(hipError_t launch_attn_decode_partial(const DecodeArgs&, int, hipStream_t))
 STAND_IN(hipError_t launch_attn_decode_combine(const DecodeArgs&, int, hipStream_t))
+STAND_IN(hipError_t decode_scratch(void**))
 #undef STAND_IN
 }  // namespace bwattn
 
@@ -126,6 +127,17 @@ int main() {
                      nullptr) == ATTN_ERR_WORKSPACE);
   EXPECT(attn_decode(&ok, 2000, addr(0), addr(1), addr(2), nullptr, addr(3), (float*)addr(4), addr(5), dws,
                      nullptr) == ATTN_ERR_INVALID_ARG);
+  // decode without a workspace: parameters beyond the static workspace are
+  // refused before any HIP call
+  EXPECT(attn_decode_noalloc_max_bytes() == (size_t(64) << 20));
+  attn_params wide = params(64, 64, 1024, 128);  // 4096 heads x 32 rows: about 96 MiB
+  EXPECT(attn_decode_workspace_bytes(&wide, 32) > attn_decode_noalloc_max_bytes());
+  EXPECT(attn_decode_noalloc(&wide, 32, addr(0), addr(1), addr(2), nullptr, addr(3), (float*)addr(4), nullptr) ==
+         ATTN_ERR_WORKSPACE);
+  EXPECT(attn_decode_noalloc(&ok, 0, addr(0), addr(1), addr(2), nullptr, addr(3), (float*)addr(4), nullptr) ==
+         ATTN_ERR_INVALID_ARG);
+  EXPECT(attn_decode_noalloc(&ok, 4, addr(0), nullptr, addr(2), nullptr, addr(3), (float*)addr(4), nullptr) ==
+         ATTN_ERR_INVALID_ARG);
   // packed cross-entropy
   packed_ce_params cp;
   std::memset(&cp, 0, sizeof(cp));

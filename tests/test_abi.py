@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(lib):
     assert {"attn_fwd", "attn_bwd", "rope_apply", "attn_workspace_bytes", "attn_status_string",
             "attn_last_error", "attn_profile_events", "attn_profile_count", "attn_decode",
             "attn_decode_workspace_bytes", "attn_fwd_f32", "attn_bwd_f32", "rope_apply_f32", "packed_ce_loss",
-            "packed_ce_workspace_bytes"} <= set(names)
+            "packed_ce_workspace_bytes", "attn_decode_noalloc", "attn_decode_noalloc_max_bytes"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -305,3 +305,20 @@ def test_binding_refuses_bad_lse_and_workspace():
         bw.packed_ce_loss(logits, tg, dlogits=t((B, S, 64), device="cpu"))
     with pytest.raises(bw.AttnError, match="workspace"):
         bw.packed_ce_loss(logits, tg, dlogits=t((B, S, 64)), workspace=t((8,), torch.uint8))
+
+
+def test_decode_noalloc_refuses_what_its_static_workspace_cannot_hold(lib):
+    """attn_decode_noalloc takes no workspace: parameters that need more than
+    its static array are refused with ATTN_ERR_WORKSPACE before any HIP
+    call; the largest decode shapes of the workloads fit."""
+    import long_context_blockwise_attn_amd as bw
+
+    V = ctypes.c_void_p
+    cap = lib.attn_decode_noalloc_max_bytes()
+    assert cap == 64 << 20
+    wide = bw.make_params(64, 64, 1024, 128)
+    assert bw.decode_workspace_bytes(wide, 32) > cap
+    rc = lib.attn_decode_noalloc(ctypes.byref(wide), 32, V(16), V(32), V(48), None, V(64), V(80), None)
+    assert rc == 3 and b"attn_decode_noalloc" in lib.attn_last_error()
+    for B, H, S, nq in ((1, 32, 1 << 20, 32), (1, 32, 1 << 20, 1), (8, 32, 1 << 16, 32), (1, 2048, 4096, 32)):
+        assert bw.decode_workspace_bytes(bw.make_params(B, H, S, 128), nq) <= cap, (B, H, S, nq)
