@@ -26,20 +26,33 @@ COMMON = [
     # no packed fp32 instructions (v_pk_*_f32) anywhere
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
-# MFMA accumulators in VGPRs (AGPRs only take spills) for the bf16 kernels,
-# whose softmax reads the score accumulators directly.  The fp32 kernels keep
-# the compiler's default AGPR accumulators: their dQ and dK/dV kernels need
-# more than 256 registers per lane, and with the VGPR form the allocator
-# there placed an MFMA source inside the MFMA's own 16-register destination.
+# MFMA accumulators in VGPRs for the bf16 kernels, whose softmax reads the
+# score accumulators directly; they fit in 256 VGPRs and spill nothing to
+# AGPRs.  The fp32 kernels keep the compiler's default AGPR accumulators:
+# their dQ and dK/dV kernels need more than 256 registers per lane, and with
+# the VGPR form they reload MFMA operands from AGPR spill slots 2 wait states
+# before the MFMA, the pattern of the only build of these sources that gave
+# results differing from call to call (tests/test_isa_guards.py checks every
+# kernel's assembly for it).
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 AGPR_ACCUMULATORS = {"attn_f32.hip"}
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJ, src + ".o")
+def _flags(src: str) -> list:
     lang = [] if src.endswith(".hip") else ["-x", "hip"]
     form = [] if src in AGPR_ACCUMULATORS else VGPR_FORM
-    cmd = [HIPCC] + COMMON + form + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    return COMMON + form + lang
+
+
+def device_asm_flags(src: str) -> list:
+    """The flags of `src`'s build for its gfx950 assembly (add -S, the source
+    and -o): the compiled kernels themselves, for reading."""
+    return _flags(src) + ["--offload-device-only"]
+
+
+def _compile(src: str) -> str:
+    obj = os.path.join(OBJ, src + ".o")
+    cmd = [HIPCC] + _flags(src) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
