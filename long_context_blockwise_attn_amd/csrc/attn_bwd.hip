@@ -94,6 +94,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
   const bool use_seg = a.seg != nullptr;
   const int32_t* segb = use_seg ? a.seg + (int64_t)b * S : nullptr;
   const int2* blkb = use_seg ? a.blk + (int64_t)b * a.nblk : nullptr;
+  const int2* t64b = use_seg ? a.t64 + (int64_t)b * a.n64p : nullptr;
 
   bf16x8 qop[NDC], dop[NDC];
   float delta;
@@ -180,7 +181,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
     bool skip = q0 >= S || (a.causal && k0 > qlast);
     bool seg_mask = false;
     if (use_seg && !skip) {
-      int2 kr = seg_range(blkb, a.nblk, k0, BK);
+      int2 kr = tile128_range(t64b, t);
       if (!ranges_meet(kr, wrange))
         skip = true;
       else
@@ -286,6 +287,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
   const bool use_seg = a.seg != nullptr;
   const int32_t* segb = use_seg ? a.seg + (int64_t)b * S : nullptr;
   const int2* blkb = use_seg ? a.blk + (int64_t)b * a.nblk : nullptr;
+  const int2* t64b = use_seg ? a.t64 + (int64_t)b * a.n64p : nullptr;
 
   bf16x8 kop[NDC], vop[NDC];
   {
@@ -362,7 +364,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
     bool skip = j0 >= S || (a.causal && ilast < j0);
     bool seg_mask = false;
     if (use_seg && !skip) {
-      int2 qr = seg_range(blkb, a.nblk, i0, BQT);
+      int2 qr = tile128_range(t64b, t);
       if (!ranges_meet(qr, wrange))
         skip = true;
       else

@@ -60,6 +60,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   const bool use_seg = a.seg != nullptr;
   const int32_t* segb = use_seg ? a.seg + (int64_t)b * S : nullptr;
   const int2* blkb = use_seg ? a.blk + (int64_t)b * a.nblk : nullptr;
+  const int2* t64b = use_seg ? a.t64 + (int64_t)b * a.n64p : nullptr;
 
   // Q operand (B of S^T = K Q^T): lane holds row `row`, d = 16 dc + 8 hl + [0,8),
   // that is the pairs 8 dc + 4 hl + [0,4), rotated to the row's position and
@@ -142,7 +143,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
     const int k0 = t * BK;
     bool seg_mask = false;
     if (use_seg) {
-      int2 kr = seg_range(blkb, a.nblk, k0, BK);
+      int2 kr = tile64_range(t64b, t);
       seg_mask = !(kr.x == kr.y && wrange.x == wrange.y && kr.x == wrange.x);
     }
     const bool lim_mask = (k0 + BK > S) || (a.causal && k0 + BK - 1 > q0);

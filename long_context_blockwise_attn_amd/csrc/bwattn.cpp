@@ -90,8 +90,8 @@ struct Plan {
   int B, H, S, D;
   bool rope, f32;
   int bq, bkv;  // own rows of the query-stationary and of the key-stationary kernel
-  int nblk, n_qtiles, n_ktiles, n_bkv, n_bq;
-  size_t off_qr, off_kr, off_delta, off_blk, off_qrange, off_krange, total;
+  int nblk, n64p, n_qtiles, n_ktiles, n_bkv, n_bq;
+  size_t off_qr, off_kr, off_delta, off_blk, off_t64, off_qrange, off_krange, total;
 };
 
 // Workspace layout of the forward (which = 0) or backward (which = 1) of the
@@ -108,6 +108,7 @@ Plan make_plan(const attn_params* p, int which, bool f32) {
   pl.bq = f32 ? (which == 0 ? kF32FwdBlockQ : kF32DqBlockQ) : kFwdBlockQ;
   pl.bkv = f32 ? kF32BwdBlockK : kBwdBlockK;
   pl.nblk = (pl.S + kSegBlock - 1) / kSegBlock;
+  pl.n64p = tile64_pitch(pl.S);
   pl.n_qtiles = (pl.S + pl.bq - 1) / pl.bq;
   pl.n_ktiles = (pl.S + kFwdBlockK - 1) / kFwdBlockK;
   pl.n_bkv = (pl.S + pl.bkv - 1) / pl.bkv;
@@ -132,6 +133,8 @@ Plan make_plan(const attn_params* p, int which, bool f32) {
   }
   pl.off_blk = off;
   off += align256((size_t)pl.B * pl.nblk * sizeof(int2));
+  pl.off_t64 = off;
+  off += align256((size_t)pl.B * pl.n64p * sizeof(int2));
   pl.off_qrange = off;
   off += align256((size_t)pl.B * pl.n_qtiles * sizeof(int2));
   if (which == 1) {
@@ -210,6 +213,9 @@ int prepare(const attn_params* p, const Plan& pl, const void* q, const void* k, 
   if (seg) {
     int2* blk = (int2*)(ws + pl.off_blk);
     int rc = hip_status(launch_block_ranges(seg, pl.B, pl.S, pl.nblk, blk, st), "segment ranges launch");
+    if (rc) return rc;
+    rc = hip_status(launch_tile64_ranges(blk, pl.B, pl.S, pl.nblk, pl.n64p, (int2*)(ws + pl.off_t64), st),
+                    "tile ranges (64 rows) launch");
     if (rc) return rc;
     TileRangeArgs t{};
     t.blk = blk;
@@ -490,6 +496,7 @@ int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, 
   a.lse = lse;
   a.seg = segment_ids;
   a.blk = segment_ids ? (const int2*)(ws + pl.off_blk) : nullptr;
+  a.t64 = segment_ids ? (const int2*)(ws + pl.off_t64) : nullptr;
   a.qrange = segment_ids ? (const int2*)(ws + pl.off_qrange) : nullptr;
   a.B = pl.B;
   a.H = pl.H;
@@ -497,6 +504,7 @@ int attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, 
   a.n_qtiles = pl.n_qtiles;
   a.n_ktiles = pl.n_ktiles;
   a.nblk = pl.nblk;
+  a.n64p = pl.n64p;
   a.causal = p->causal;
   a.chunk_tiles = p->kv_chunk / kFwdBlockK;
   a.pos = positions;
@@ -543,6 +551,7 @@ int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v, 
   a.seg = segment_ids;
   a.pos = positions;
   a.blk = segment_ids ? (const int2*)(ws + pl.off_blk) : nullptr;
+  a.t64 = segment_ids ? (const int2*)(ws + pl.off_t64) : nullptr;
   a.qrange = segment_ids ? (const int2*)(ws + pl.off_qrange) : nullptr;
   a.krange = segment_ids ? (const int2*)(ws + pl.off_krange) : nullptr;
   a.B = pl.B;
@@ -551,6 +560,7 @@ int attn_bwd(const attn_params* p, const void* q, const void* k, const void* v, 
   a.n_qtiles = pl.n_qtiles;
   a.n_ktiles = pl.n_ktiles;
   a.nblk = pl.nblk;
+  a.n64p = pl.n64p;
   a.n_bkv = pl.n_bkv;
   a.n_bq = pl.n_bq;
   a.scale = scale_of(p);

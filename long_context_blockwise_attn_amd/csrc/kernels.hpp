@@ -49,9 +49,10 @@ struct FwdArgs {
   float* lse;          // natural log, [B,H,S]
   const int32_t* seg;  // [B,S] or null
   const int2* blk;     // segment ranges per 32 rows, or null
+  const int2* t64;     // segment ranges per 64-row tile, [B, n64p], or null
   const int2* qrange;  // [B, n_qtiles] K/V tile range, or null
   int B, H, S;
-  int n_qtiles, n_ktiles, nblk;
+  int n_qtiles, n_ktiles, nblk, n64p;
   int causal;
   int chunk_tiles;     // ring chunk in K/V tiles; 0 = natural order
   const int32_t* pos;  // [B,S] or null (pos = s), for the query rows' RoPE
@@ -74,10 +75,11 @@ struct BwdArgs {
   const int32_t* seg;
   const int32_t* pos;  // [B,S] or null, for the RoPE backward
   const int2* blk;
+  const int2* t64;      // segment ranges per 64-row tile, [B, n64p], or null
   const int2* qrange;   // per query tile (dQ kernel): K/V tile range
   const int2* krange;   // per key tile (dK/dV kernel): query tile range
   int B, H, S;
-  int n_qtiles, n_ktiles, nblk;
+  int n_qtiles, n_ktiles, nblk, n64p;
   int n_bkv, n_bq;     // dK/dV kernel: key tiles of kBwdBlockK and query tiles of kBwdBlockQ
   float scale;         // softmax scale
   float dk_scale;      // scale / (scale log2 e): dK' from the scaled query rows
@@ -179,6 +181,11 @@ hipError_t launch_attn_fwd_f32(const F32Args& a, int D, hipStream_t st);
 hipError_t launch_attn_bwd_dq_f32(const F32Args& a, int D, hipStream_t st);
 hipError_t launch_attn_bwd_dkdv_f32(const F32Args& a, int D, hipStream_t st);
 hipError_t launch_block_ranges(const int32_t* seg, int B, int S, int nblk, int2* out, hipStream_t st);
+// Row pitch of the per-64-row tile range table: n64 = ceil(S / 64) entries
+// and at least one more, an even count (16-byte aligned rows), the entries
+// past the last tile repeating it, so a pair of entries can be read at once.
+inline int tile64_pitch(int S) { return (((S + 63) / 64) + 2) & ~1; }
+hipError_t launch_tile64_ranges(const int2* blk, int B, int S, int nblk, int n64p, int2* out, hipStream_t st);
 hipError_t launch_tile_ranges(const TileRangeArgs& a, hipStream_t st);
 hipError_t launch_attn_fwd(const FwdArgs& a, int D, hipStream_t st);
 hipError_t launch_attn_bwd_dq(const BwdArgs& a, int D, hipStream_t st);

@@ -117,6 +117,23 @@ __global__ void block_range_kernel(const int32_t* seg, int B, int S, int nblk, i
   out[tid] = make_int2(mn, mx);
 }
 
+// Min and max segment id of every 64-row tile (from the 32-row blocks), in
+// rows of n64p entries; entries past the last tile repeat it.
+__global__ void tile64_range_kernel(const int2* blk, int B, int S, int nblk, int n64p, int2* out) {
+  int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (tid >= (int64_t)B * n64p) return;
+  const int b = (int)(tid / n64p);
+  const int n64 = (S + 63) / 64;
+  const int t = min((int)(tid % n64p), n64 - 1);
+  const int2* br = blk + (int64_t)b * nblk;
+  int2 r = br[2 * t];
+  if (2 * t + 1 < nblk) {
+    const int2 u = br[2 * t + 1];
+    r = make_int2(min(r.x, u.x), max(r.y, u.y));
+  }
+  out[tid] = r;
+}
+
 __device__ __forceinline__ int2 rows_range(const int2* br, int nblk, int r0, int rows) {
   int b0 = r0 >> 5, b1 = min(nblk, (r0 + rows + 31) >> 5);
   int2 acc = br[b0];
@@ -229,6 +246,14 @@ hipError_t launch_block_ranges(const int32_t* seg, int B, int S, int nblk, int2*
   int threads = 256;
   hipLaunchKernelGGL(block_range_kernel, dim3((unsigned)((total + threads - 1) / threads)), dim3(threads), 0, st,
                      seg, B, S, nblk, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile64_ranges(const int2* blk, int B, int S, int nblk, int n64p, int2* out, hipStream_t st) {
+  int64_t total = (int64_t)B * n64p;
+  int threads = 256;
+  hipLaunchKernelGGL(tile64_range_kernel, dim3((unsigned)((total + threads - 1) / threads)), dim3(threads), 0, st,
+                     blk, B, S, nblk, n64p, out);
   return hipGetLastError();
 }
 

@@ -209,6 +209,15 @@ __device__ __forceinline__ int2 seg_range(const int2* blk, int nblk, int r0, int
   return acc;
 }
 
+// Segment range of 64-row tile t, and of 128-row tile t (64-row tiles 2t and
+// 2t + 1, one 16-byte scalar load), from a row of the per-64-row table (its
+// padding entries make the pair read safe at the last tile).
+__device__ __forceinline__ int2 tile64_range(const int2* t64b, int t) { return t64b[uniform(t)]; }
+__device__ __forceinline__ int2 tile128_range(const int2* t64b, int t) {
+  const int4 v = *(const int4*)(t64b + 2 * uniform(t));
+  return make_int2(min(v.x, v.z), max(v.y, v.w));
+}
+
 // Walk over tiles [lo, hi) of the streamed side.  ct > 0 selects ring order:
 // tiles are grouped in chunks of ct; the walk visits the own chunk r first,
 // then r + dir, r + 2 dir, ... (mod nc), tiles ascending inside each chunk.

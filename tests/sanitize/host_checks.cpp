@@ -32,6 +32,7 @@ STAND_IN(hipError_t launch_attn_bwd_dq_f32(const F32Args&, int, hipStream_t))
 STAND_IN(hipError_t launch_attn_bwd_dkdv_f32(const F32Args&, int, hipStream_t))
 STAND_IN(hipError_t launch_block_ranges(const int32_t*, int, int, int, int2*, hipStream_t))
 STAND_IN(hipError_t launch_tile_ranges(const TileRangeArgs&, hipStream_t))
+STAND_IN(hipError_t launch_tile64_ranges(const int2*, int, int, int, int, int2*, hipStream_t))
 STAND_IN(hipError_t launch_attn_fwd(const FwdArgs&, int, hipStream_t))
 STAND_IN(hipError_t launch_attn_bwd_dq(const BwdArgs&, int, hipStream_t))
 STAND_IN(hipError_t launch_attn_bwd_dkdv(const BwdArgs&, int, hipStream_t))
