@@ -169,3 +169,49 @@ def test_full_size_bitwise_reproducible(torch_cuda, name):
         assert torch.equal(x, y), n
     del q, k, v, do, runs
     torch.cuda.empty_cache()
+
+
+# workload, heads compared on every row for the forward, heads for the backward
+EVERY_ROW = [
+    ("llama7b_32k", (0, 17), (9,)),
+    ("packing_128k", (3, 30), (14,)),
+    ("video_text_256k", (6, 25), ()),
+]
+
+
+@pytest.mark.parametrize("name,fwd_heads,bwd_heads", EVERY_ROW)
+def test_full_size_every_row(oracle, torch_cuda, name, fwd_heads, bwd_heads):
+    """The whole workload on the GPU, and whole heads against the oracle:
+    O and LSE on every row of two heads, and dq, dk, dv on every row of one
+    head (the bf16 path, the benchmark's parameters)."""
+    import long_context_blockwise_attn_amd as bw
+    from long_context_blockwise_attn_amd.inputs import WORKLOADS, make_qkv, packing
+
+    torch = torch_cuda
+    w = WORKLOADS[name]
+    seg, pos, lengths = packing(w)
+    q, k, v, do = make_qkv(w, device="cuda", with_grad_out=True)
+    dseg = None if seg is None else torch.from_numpy(seg).cuda()
+    dpos = torch.from_numpy(pos).cuda()
+    print("every row %s: B%d H%d S%d D%d, forward heads %s, backward heads %s" % (
+        name, w.batch, w.heads, w.seqlen, w.head_dim, fwd_heads, bwd_heads), flush=True)
+    o, lse = bw.attn_fwd(q, k, v, dseg, dpos, theta=w.theta, causal=w.causal, kv_chunk=w.kv_chunk)
+    grads = None
+    if bwd_heads:
+        grads = bw.attn_bwd(q, k, v, o, lse, do, dseg, dpos, theta=w.theta, causal=w.causal, kv_chunk=w.kv_chunk)
+    torch.cuda.synchronize()
+    for h in fwd_heads:
+        qh, kh, vh = head64(q, h), head64(k, h), head64(v, h)
+        ro, rlse = oracle.attn_fwd(qh, kh, vh, seg, pos, theta=w.theta, causal=w.causal)
+        eo = assert_parity(o[:, h:h + 1], ro, "%s h%d O" % (name, h))
+        el = assert_parity(lse[:, h:h + 1].cpu().numpy(), rlse, "%s h%d LSE" % (name, h))
+        print("  head %d: O, LSE on all %d rows, (max, mean) abs errors %s %s" % (h, w.seqlen, eo, el), flush=True)
+    for h in bwd_heads:
+        dq, dk, dv = grads
+        rdq, rdk, rdv = oracle.attn_bwd(head64(q, h), head64(k, h), head64(v, h), head64(do, h), seg, pos,
+                                        theta=w.theta, causal=w.causal)
+        e = [assert_parity(g[:, h:h + 1], r, "%s h%d %s" % (name, h, n))
+             for n, g, r in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv))]
+        print("  head %d: dq, dk, dv on all %d rows, (max, mean) abs errors %s" % (h, w.seqlen, e), flush=True)
+    del q, k, v, do, o, lse, grads
+    torch.cuda.empty_cache()
