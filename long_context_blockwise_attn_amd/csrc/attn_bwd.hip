@@ -406,12 +406,20 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
           dp = mfma32(da, vop[dc], dp);
         }
         if (need_mask) {
+          // rows i0 + 32 qg + 8 rq + 4 hl + e in registers s[4 rq + e]; their
+          // segment ids, when the tile needs them, read four at a time
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            int ri = 32 * qg + 8 * (r >> 2) + 4 * hl + (r & 3);
-            int i = i0 + ri;
-            const bool vis = i < S && (!a.causal || j <= i) && (!seg_mask || ((const int*)st)[2 * BQT + ri] == segk);
-            s[r] = vis ? s[r] : kNegInf;
+          for (int rq = 0; rq < 4; ++rq) {
+            const int ri = 32 * qg + 8 * rq + 4 * hl;
+            int4 sq = make_int4(segk, segk, segk, segk);
+            if (uniform(seg_mask)) sq = *(const int4*)((const int*)st + 2 * BQT + ri);
+            const int sq_[4] = {sq.x, sq.y, sq.z, sq.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int i = i0 + ri + e;
+              const bool vis = i < S && (!a.causal || j <= i) && sq_[e] == segk;
+              s[4 * rq + e] = vis ? s[4 * rq + e] : kNegInf;
+            }
           }
         }
         // P = exp(S scale - LSE) and dS = P (dP - Delta)
