@@ -101,18 +101,38 @@ KERNEL_SYMBOLS = {"fwd": "attn_fwd_kernel", "bwd_dq": "attn_bwd_dq_kernel", "bwd
                   "packed_ce": "ce_row_kernel"}
 
 
-def kernel_source_hash():
-    """sha256 over the HIP/C++ sources of the library: a traffic record is
-    only used while the kernels are the ones it was measured on."""
+# the sources each measured kernel is built from (with the shared headers
+# and build flags): a stored record applies while these hash the same
+_SHARED_SOURCES = ["common.hpp", "kernels.hpp", "tile.hpp", "prep.hip", "../build.py"]
+KERNEL_SOURCES = {
+    "attention": ["attn_fwd.hip", "attn_bwd.hip"],
+    "f32": ["attn_f32.hip"],
+    "decode": ["attn_decode.hip"],
+    "packed_ce": ["packed_ce.hip"],
+}
+
+
+def kernel_family(kernel):
+    if kernel.endswith("_f32"):
+        return "f32"
+    if kernel.startswith("decode"):
+        return "decode"
+    if kernel == "packed_ce":
+        return "packed_ce"
+    return "attention"
+
+
+def kernel_source_hash(family):
+    """sha256 over the sources of one kernel family: a traffic or counter
+    record is only used while the kernels are the ones it was measured on."""
     import hashlib
 
     d = os.path.join(ROOT, "long_context_blockwise_attn_amd", "csrc")
     h = hashlib.sha256()
-    for name in sorted(os.listdir(d)):
-        if name.endswith((".hip", ".hpp", ".cpp", ".h")):
-            h.update(name.encode())
-            with open(os.path.join(d, name), "rb") as f:
-                h.update(f.read())
+    for name in KERNEL_SOURCES[family] + _SHARED_SOURCES:
+        h.update(name.encode())
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()
 
 
@@ -139,7 +159,7 @@ def write_traffic_record(workload, fetch_csv, write_csv, copy_mib, command):
     runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by the
     factor that makes the last plain copy of the run (copy_mib MiB read and
     written) read exactly its size."""
-    rec = {"workload": workload, "source_sha256": kernel_source_hash(), "command": command, "kernels": {}}
+    rec = {"workload": workload, "command": command, "kernels": {}}
     copy_bytes = float(copy_mib) * (1 << 20)
     for counter, path, key in (("FETCH_SIZE", fetch_csv, "read"), ("WRITE_SIZE", write_csv, "write")):
         rows = counter_rows(path, counter)
@@ -156,8 +176,9 @@ def write_traffic_record(workload, fetch_csv, write_csv, copy_mib, command):
                 k["%s_counter_kib" % key] = float(np.mean(vals))
                 k["%s_bytes" % key] = float(np.mean(vals)) * 1024.0 * factor
                 k["dispatches"] = len(vals)
-    for k in rec["kernels"].values():
+    for name, k in rec["kernels"].items():
         k["traffic_bytes"] = k.get("read_bytes", 0.0) + k.get("write_bytes", 0.0)
+        k["source_sha256"] = kernel_source_hash(kernel_family(name))
     with open(traffic_path(workload), "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec, indent=1))
@@ -171,10 +192,10 @@ def load_traffic(workload, kernel):
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != kernel_source_hash():
-        return None
     k = rec.get("kernels", {}).get(kernel)
-    return None if k is None else k.get("traffic_bytes")
+    if k is None or k.get("source_sha256") != kernel_source_hash(kernel_family(kernel)):
+        return None
+    return k.get("traffic_bytes")
 
 
 def counters_path(workload):
@@ -201,8 +222,7 @@ def write_counter_record(workload, csvs, command, simds=1024, xcds=8):
         FLOPs."""
     import csv
 
-    rec = {"workload": workload, "source_sha256": kernel_source_hash(), "command": command, "simds": simds,
-           "xcds": xcds, "kernels": {}}
+    rec = {"workload": workload, "command": command, "simds": simds, "xcds": xcds, "kernels": {}}
     for path in csvs:
         rows, durs = {}, {}
         with open(path) as fh:
@@ -218,7 +238,8 @@ def write_counter_record(workload, csvs, command, simds=1024, xcds=8):
                     k.setdefault("dispatches", {})[counter] = len(vals)
                     k.setdefault("pmc_run_ms", {})[os.path.basename(path)] = 1e3 * float(
                         np.mean(list(durs[kname].values())))
-    for k in rec["kernels"].values():
+    for name, k in rec["kernels"].items():
+        k["source_sha256"] = kernel_source_hash(kernel_family(name))
         ms = float(np.mean(list(k["pmc_run_ms"].values())))
         if "GRBM_GUI_ACTIVE" in k:
             cycles = k["GRBM_GUI_ACTIVE"] / xcds
@@ -242,10 +263,8 @@ def load_counters(workload, kernel, avg_ms, peak):
             rec = json.load(fh)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != kernel_source_hash():
-        return None
     k = rec.get("kernels", {}).get(kernel)
-    if not k:
+    if not k or k.get("source_sha256") != kernel_source_hash(kernel_family(kernel)):
         return None
     dtype = "f32" if kernel.endswith("_f32") else "bf16"
     out = {"source": os.path.relpath(counters_path(workload), ROOT)}
