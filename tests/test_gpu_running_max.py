@@ -7,7 +7,9 @@ score MFMAs.  Random inputs almost never need a raise after the first tile,
 so in these cases every key before S/3 carries a bias of about -12 in log2
 units (one dimension: q = C, k = -24): with the forward walking tiles in
 increasing order (the decode each chunk so), every row that reaches the
-unbiased keys raises its max once, mid-walk.  The bias is large but its
+unbiased keys raises its max once, mid-walk; in a second set the keys fall
+in four equal runs biased by about -36, -24, -12 and 0, so a row raises its
+max up to three times.  The bias is large but its
 keys' probabilities are tiny, so the scores that matter stay of the usual
 size.  Forward and decode (the kernels with a running max) against the
 oracle, and the backward, which recomputes P from the forward's LSE.
@@ -66,7 +68,10 @@ def bias_query_value(D):
     return float(cand[i])
 
 
-def rising_case(S, D, seed, with_grad_out=False):
+def rising_case(S, D, seed, with_grad_out=False, stairs=1):
+    """stairs = 1: keys before S/3 biased by about -12 (log2 units), the rest
+    not.  stairs = n > 1: n + 1 equal runs of keys biased by -12n, ..., -12,
+    0, so that a row raises its max once on entering each later run."""
     from long_context_blockwise_attn_amd.inputs import random_case
 
     (q, k, v, do), _, pos = random_case(1, 2, S, D, seed)
@@ -74,8 +79,13 @@ def rising_case(S, D, seed, with_grad_out=False):
     q[..., bd] = bias_query_value(D)
     q[..., bd + 1] = 0.0
     k[..., bd + 1] = 0.0
-    k[..., : S // 3, bd] = -24.0
-    k[..., S // 3:, bd] = 0.0
+    if stairs == 1:
+        k[..., : S // 3, bd] = -24.0
+        k[..., S // 3:, bd] = 0.0
+    else:
+        edges = [S * r // (stairs + 1) for r in range(stairs + 2)]
+        for r in range(stairs + 1):
+            k[..., edges[r]:edges[r + 1], bd] = -24.0 * (stairs - r)
     return (q, k, v, pos, do) if with_grad_out else (q, k, v, pos)
 
 
@@ -107,6 +117,13 @@ def test_inputs_raise_the_running_max():
         # every row that reaches the unbiased keys raises once; none before
         assert (r[: 1000 // 3] == 0).all()
         assert (r[1000 // 3 + 64:] >= 1).mean() > 0.9
+        q, k, _, _ = rising_case(2000, D, seed=6, stairs=3)
+        r = raises_per_row(q, k, causal=True)
+        # a row raises on entering each later run of keys: up to three times
+        for n in range(4):
+            lo = 500 * n
+            assert (r[lo:lo + 500] <= n).all()
+            assert (r[lo + 64:lo + 500] == n).mean() > 0.9
 
 
 @pytest.mark.gpu
@@ -155,6 +172,44 @@ def test_decode_with_raised_max(oracle, torch_cuda, theta):
     kc, vc = k.cuda(), v.cuda()
     kcache = bw.rope_apply(kc, dpos, theta=theta) if theta > 0 else kc
     o, lse = bw.attn_decode(q[:, :, S - nq:].contiguous().cuda(), kcache, vc, None, theta=theta)
+    torch.cuda.synchronize()
+    rows = np.arange(S - nq, S, dtype=np.int64)
+    ro, rlse = oracle.attn_fwd(to64(q), to64(k), to64(v), None, pos, theta=theta, causal=True, rows=rows)
+    assert_parity(o, ro, "O")
+    assert_parity(lse.cpu().numpy(), rlse, "LSE")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("D,theta,kv_chunk", [(128, 0.0, 0), (128, 1e6, 0), (64, 1e6, 0), (128, 1e6, 512)])
+def test_fwd_with_several_raises(oracle, torch_cuda, D, theta, kv_chunk):
+    """Rows that raise their running max up to three times in one walk (the
+    forward is the kernel with a running max; the backward recomputes P from
+    the LSE and has none)."""
+    import long_context_blockwise_attn_amd as bw
+
+    torch = torch_cuda
+    S = 2000
+    q, k, v, pos = rising_case(S, D, seed=6, stairs=3)
+    print("stair keys S%d D%d theta %g chunk %d" % (S, D, theta, kv_chunk), flush=True)
+    dpos = torch.from_numpy(pos).cuda()
+    o, lse = bw.attn_fwd(q.cuda(), k.cuda(), v.cuda(), None, dpos, theta=theta, causal=True, kv_chunk=kv_chunk)
+    torch.cuda.synchronize()
+    ro, rlse = oracle.attn_fwd(to64(q), to64(k), to64(v), None, pos, theta=theta, causal=True)
+    assert_parity(o, ro, "O")
+    assert_parity(lse.cpu().numpy(), rlse, "LSE")
+
+
+@pytest.mark.gpu
+def test_decode_with_several_raises(oracle, torch_cuda):
+    import long_context_blockwise_attn_amd as bw
+
+    torch = torch_cuda
+    S, nq, theta = 8192, 4, 1e6
+    q, k, v, pos = rising_case(S, 128, seed=8, stairs=3)
+    print("decode stair keys S%d n_q %d theta %g" % (S, nq, theta), flush=True)
+    dpos = torch.from_numpy(pos).cuda()
+    kcache = bw.rope_apply(k.cuda(), dpos, theta=theta)
+    o, lse = bw.attn_decode(q[:, :, S - nq:].contiguous().cuda(), kcache, v.cuda(), None, theta=theta)
     torch.cuda.synchronize()
     rows = np.arange(S - nq, S, dtype=np.int64)
     ro, rlse = oracle.attn_fwd(to64(q), to64(k), to64(v), None, pos, theta=theta, causal=True, rows=rows)
