@@ -101,14 +101,15 @@ KERNEL_SYMBOLS = {"fwd": "attn_fwd_kernel", "bwd_dq": "attn_bwd_dq_kernel", "bwd
                   "packed_ce": "ce_row_kernel"}
 
 
-# the sources each measured kernel is built from (with the shared headers
-# and build flags): a stored record applies while these hash the same
-_SHARED_SOURCES = ["common.hpp", "kernels.hpp", "tile.hpp", "prep.hip", "../build.py"]
+# the sources each measured kernel family is built from: its own file, the
+# headers it includes, the pre-pass whose tables it reads, and the build
+# flags.  A stored record applies while these hash the same.
+_HEADERS = ["common.hpp", "kernels.hpp"]
 KERNEL_SOURCES = {
-    "attention": ["attn_fwd.hip", "attn_bwd.hip"],
-    "f32": ["attn_f32.hip"],
-    "decode": ["attn_decode.hip"],
-    "packed_ce": ["packed_ce.hip"],
+    "attention": ["attn_fwd.hip", "attn_bwd.hip", "prep.hip", "tile.hpp"] + _HEADERS + ["../build.py"],
+    "f32": ["attn_f32.hip", "prep.hip", "tile.hpp"] + _HEADERS + ["../build.py"],
+    "decode": ["attn_decode.hip", "prep.hip", "tile.hpp"] + _HEADERS + ["../build.py"],
+    "packed_ce": ["packed_ce.hip"] + _HEADERS + ["../build.py"],
 }
 
 
@@ -129,7 +130,7 @@ def kernel_source_hash(family):
 
     d = os.path.join(ROOT, "long_context_blockwise_attn_amd", "csrc")
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES[family] + _SHARED_SOURCES:
+    for name in KERNEL_SOURCES[family]:
         h.update(name.encode())
         with open(os.path.join(d, name), "rb") as f:
             h.update(f.read())

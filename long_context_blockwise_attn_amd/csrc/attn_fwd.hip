@@ -127,6 +127,12 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   };
   // vector-memory instructions this wave issues per tile
   const int per_tile = kfill.count() + vfill.count() + (use_seg && w == 0 ? 1 : 0);
+  // the fewest any wave issues: a compile-time wait count.  Waiting until
+  // that many are in flight completes the wave's loads of the older of two
+  // positions (a wave with more loads also waits for a few of the newer
+  // position, issued a step earlier); a wait on the exact count would need a
+  // branch table, whose scalar code cost ~3% of the forward's time.
+  constexpr int kLeastPerTile = KT::kBlocks / NW + VR::kBlocks / NW;
 
   // --- per-tile pieces -----------------------------------------------------
   // S^T - m of the tile in `buf` (log2 units): s[kg] holds keys
@@ -288,7 +294,10 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
 
     // wait for position k+2 (k+3 may be in flight), barrier, issue k+4
     auto refill = [&](int k) {
-      wait_vmem_le((ahead.t >= 0 && ahead_pos >= k + 3) ? per_tile : 0);
+      if (ahead.t >= 0 && ahead_pos >= k + 3)
+        wait_vmem_le<kLeastPerTile>();
+      else
+        wait_vmem_le<0>();
       __syncthreads();
       if (ahead.t >= 0) ahead.next();
       if (ahead.t >= 0) {

@@ -142,6 +142,13 @@ constexpr int kSchedVALU = 0x002, kSchedMFMA = 0x008, kSchedDSRead = 0x100;
 
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0); }
 
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
 // Wait until at most n vector-memory operations of this wave are in flight
 // (n uniform across the wave, 0 <= n < 64).  s_waitcnt takes an immediate,
 // hence the table; expcnt and lgkmcnt are left at their maxima.
@@ -368,7 +375,10 @@ __device__ __forceinline__ void run_pipeline_mid(TileWalk walk, int per_tile, ch
     nx.next();
     compute(uniform(walk.t), (const char*)(base + cur * stride), issue_next);
     if (nx.t >= 0) --issued;
-    wait_vmem_le(issued * per_tile);
+    if constexpr (NSTAGE == 2)
+      wait_vmem_le<0>();  // only tile t + 1's loads can be in flight
+    else
+      wait_vmem_le(issued * per_tile);
     __syncthreads();
     cur = cur + 1 == NSTAGE ? 0 : cur + 1;
     walk = nx;
