@@ -166,7 +166,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
   const uint16_t* vh = a.v + base;
   TileFill<BK, D / 8, NW, 3> rfill;  // K and V rows
   rfill.init(D * 2, tid);
-  auto load = [&](int t, char* buf) {
+  auto load = [&](int t, char* buf, int part) {
+    if (part != 0) return;  // this kernel issues a tile's loads in one go
     const uint32_t rbytes = (uint32_t)min(S - t * BK, BK) * D * 2;  // rows past S read zero
     rfill.fill(kh + (int64_t)t * BK * D, rbytes, buf);
     rfill.fill(vh + (int64_t)t * BK * D, rbytes, buf + KT::kBytes);
@@ -187,7 +188,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
       else
         seg_mask = !(kr.x == kr.y && wrange.x == wrange.y && kr.x == wrange.x);
     }
-    if (uniform(skip)) issue();  // a skipped tile still issues this wave's loads
+    if (uniform(skip)) { issue(0); issue(1); }  // a skipped tile still issues this wave's loads
     if (!skip) {
       const char* ktl = buf;
       const char* vtl = buf + KT::kBytes;
@@ -240,7 +241,10 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdArgs a) {
         lds_mfma_pipe<2 * NDG, 6>(
             [&](int i) { return KT::read_tr(ktl, 32 * kg + 16 * (i / NDG), 32 * (i % NDG), lane); },
             [&](int i, bf16x8 x) { dq[i % NDG] = mfma32(x, dsk[i / NDG], dq[i % NDG]); });
-        if (kg == BK / 64 - 1) issue();  // the loads of tile t + 1, in the middle of the tile
+        if (kg == BK / 64 - 1) {  // the loads of tile t + 1, in the middle of the tile
+          issue(0);
+          issue(1);
+        }
       }
     }
   };
@@ -341,9 +345,12 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
   // segment id), the statistics fetched by wave 0
   TileFill<BQT, D / 8, NW, 3> rfill;  // Q and dO rows
   rfill.init(D * 2, tid);
-  auto load = [&](int t, char* buf) {
+  auto load = [&](int t, char* buf, int part) {
     const uint32_t rbytes = (uint32_t)min(S - t * BQT, BQT) * D * 2;  // rows past S read zero
-    rfill.fill(qh + (int64_t)t * BQT * D, rbytes, buf);
+    if (part == 0) {
+      rfill.fill(qh + (int64_t)t * BQT * D, rbytes, buf);
+      return;
+    }
     rfill.fill(dh + (int64_t)t * BQT * D, rbytes, buf + QT::kBytes);
     // statistics: wave 0 -LSE log2e, wave 1 -Delta, wave 2 the segment ids
     if (w == 0) {
@@ -370,7 +377,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
       else
         seg_mask = !(qr.x == qr.y && wrange.x == wrange.y && qr.x == wrange.x);
     }
-    if (uniform(skip)) issue();  // a skipped tile still issues this wave's loads
+    if (uniform(skip)) { issue(0); issue(1); }  // a skipped tile still issues this wave's loads
     if (!skip) {
       const char* qtl = buf;
       const char* dtl = buf + QT::kBytes;
@@ -457,7 +464,11 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdArgs a) {
             dk[dg] = mfma32(qta, dsk[c], dk[dg]);
           }
         }
-        if (qg == BQT / 64 - 1) issue();  // the loads of tile t + 1, in the middle of the tile
+        // the loads of tile t + 1 in two parts, Q after the first 32 rows and
+        // dO with the statistics after the second: one burst of every wave's
+        // loads stalled each wave longer (dK/dV -1% split)
+        if (qg == 0) issue(0);
+        if (qg == 1) issue(1);
       }
     }
   };

@@ -107,8 +107,11 @@ struct TileFill {
   static constexpr int kPer = (kBlocks + NW - 1) / NW;
   uint32_t voff[kPer];
   int w;
+  static_assert((NW & (NW - 1)) == 0, "power-of-two wave count");
   __device__ void init(uint32_t row_bytes, int tid) {
-    w = uniform(tid >> 6);
+    // tid < NW * 64: the mask changes nothing but tells the compiler that
+    // w < NW, so the per-block bounds tests of fill() that always pass fold
+    w = uniform(tid >> 6) & (NW - 1);
     const int lane = tid & 63;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
@@ -341,33 +344,37 @@ __device__ __forceinline__ void run_pipeline(TileWalk walk, int per_tile, char* 
 
 // As run_pipeline<NSTAGE, true>, but the loads of tile t + NSTAGE - 1 (into
 // the slot of tile t - 1, free since the last barrier) go out from inside
-// compute(t, buf, issue), which calls issue() exactly once per tile, at a
-// point of its choosing: a wave that issues between its own MFMA phases
-// takes the load path's stall while the other wave of its SIMD keeps the
-// matrix unit busy.
+// compute(t, buf, issue), which calls issue(0) and then issue(1) exactly once
+// each per tile, at points of its choosing; issue(p) calls load(t', buf', p)
+// for the next tile.  A wave that issues between its own MFMA phases takes
+// the load path's stall while the other wave of its SIMD keeps the matrix
+// unit busy, and two parts spread the stall.
 template <int NSTAGE, class Load, class Compute>
 __device__ __forceinline__ void run_pipeline_mid(TileWalk walk, int per_tile, char* base, int stride, Load&& load,
                                                  Compute&& compute) {
   static_assert(NSTAGE >= 2, "the slot of tile t - 1 takes tile t + NSTAGE - 1");
   TileWalk ahead = walk;
   int issued = 0;
-  if (walk.t >= 0) load(uniform(walk.t), base);
+  if (walk.t >= 0) { load(uniform(walk.t), base, 0); load(uniform(walk.t), base, 1); }
   for (int st = 1; st < NSTAGE - 1; ++st) {
     if (ahead.t >= 0) ahead.next();
     if (ahead.t >= 0) {
-      load(uniform(ahead.t), base + st * stride);
+      load(uniform(ahead.t), base + st * stride, 0);
+      load(uniform(ahead.t), base + st * stride, 1);
       ++issued;
     }
   }
   wait_vmem_le(issued * per_tile);
   __syncthreads();
   int cur = 0;
-  auto issue_next = [&]() {
-    if (ahead.t >= 0) ahead.next();
+  auto issue_next = [&](int part) {
+    if (part == 0) {
+      if (ahead.t >= 0) ahead.next();
+      if (ahead.t >= 0) ++issued;
+    }
     if (ahead.t >= 0) {
       const int fill = cur == 0 ? NSTAGE - 1 : cur - 1;
-      load(uniform(ahead.t), base + fill * stride);
-      ++issued;
+      load(uniform(ahead.t), base + fill * stride, part);
     }
   };
   while (walk.t >= 0) {
