@@ -255,12 +255,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   // Barrier G_j: group 0 runs the matrix phase of step k between G_2k and
   // G_2k+1, group 1 between G_2k+1 and G_2k+2.  Tile position p lives in ring
   // slot p % 4; it is read from G_2p-2 (K of p in the matrix phase of step
-  // p-1) until G_2p+2 (V of p in group 1's matrix phase of step p); its K
-  // part is free from G_2p, its V part from G_2p+2.  So group 0 issues
-  // position k+4 right after G_2k+2, group 1 issues its K rows between
-  // G_2k+1 and G_2k+2 and its V rows right after G_2k+2, and before G_2k+2
-  // each wave waits for its loads of position k+2 (later ones may still be
-  // in flight).
+  // p-1) until G_2p+2 (V of p in group 1's matrix phase of step p).  So each
+  // wave issues position k+4 right after G_2k+2 and, before G_2k+2, waits for
+  // its loads of position k+2 (only k+3 may still be in flight).
   static_assert(NW == 8 && NSTAGE == 4, "two groups of four waves, four-slot ring");
   const int grp = uniform(w >> 2);
   auto slot = [&](int p) { return smem + (p & (NSTAGE - 1)) * BUF; };
@@ -308,33 +305,6 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
         load(uniform(ahead.t), slot(ahead_pos));
       }
     };
-    // Group 1 issues the K rows of position k+4 before that barrier, right
-    // after its matrix phase: the K part of their slot was last read by the
-    // scores of step k-1, the V part is read until the barrier.  This moves
-    // half of its loads out of the half step it spends in the vector phase
-    // (forward -1.7% at 128K packing).  Its waves load no tail blocks and no
-    // segment ids, so their counts are exact constants.
-    static_assert(KT::kBlocks % NW <= NW / 2 && VR::kBlocks % NW <= NW / 2, "tail blocks stay in group 0");
-    constexpr int kK1 = KT::kBlocks / NW, kV1 = VR::kBlocks / NW;
-    auto refill1 = [&](int k) {
-      TileWalk nxt = ahead;
-      if (nxt.t >= 0) nxt.next();
-      const int t4 = uniform(nxt.t);
-      if (t4 >= 0) {
-        kfill.fill(kh + (int64_t)t4 * BK * D, (uint32_t)min(S - t4 * BK, BK) * D * 2, slot(ahead_pos + 1));
-        wait_vmem_le<2 * kK1 + kV1>();  // K, V of k+3 and K of k+4 in flight
-      } else if (ahead.t >= 0 && ahead_pos >= k + 3) {
-        wait_vmem_le<kK1 + kV1>();
-      } else {
-        wait_vmem_le<0>();
-      }
-      __syncthreads();
-      ahead = nxt;
-      if (t4 >= 0) {
-        ++ahead_pos;
-        vfill.fill(vh + (int64_t)t4 * BK * D, (uint32_t)min(S - t4 * BK, BK) * D * 2, slot(ahead_pos) + KT::kBytes);
-      }
-    };
 
     int k = 0;
     while (walk.t >= 0) {
@@ -347,7 +317,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
       if (grp == 0)
         __syncthreads();
       else
-        refill1(k);
+        refill(k);
       if (more) {
         mask(uniform(w1.t), slot(k + 1), s_next);
         rescale(tile_max(s_next), s_next);
