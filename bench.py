@@ -88,6 +88,7 @@ def cpu_baseline(w, q, k, v, do, seg, pos, budget_s):
         "cpu_model": model,
         "host_cores_available": avail,
         "kind": "oracle",
+        "extrapolated": True,  # a rate measured on the sample, taken for the whole workload
         "sample": "fwd+bwd of %d evenly spaced query rows of head 0 (of %d rows x %d heads), %.1f s; "
                   "credited 14*D FLOPs per visible pair of those rows" % (len(rows), S, w.heads, dt),
         "seconds": dt,
@@ -393,7 +394,7 @@ def decode_bench(args, w):
         head_bytes = 2.0 * S * D * 2 + 2.0 * nq * D * 2 + nq * 4
         model, avail = host_cpu()
         cpu = {"value": reps * head_bytes / dt / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
-               "cpu_model": model, "host_cores_available": avail, "kind": "oracle",
+               "cpu_model": model, "host_cores_available": avail, "kind": "oracle", "extrapolated": True,
                "sample": "%d oracle calls on head 0 of %d (the n_q rows against its whole cache, K rotated inside), "
                          "%.1f s; credited that head's bf16 cache bytes per call" % (reps, H, dt),
                "seconds": dt}
@@ -497,7 +498,7 @@ def packed_ce_bench(args, w):
         sample_bytes = 2.0 * nl * V + 2.0 * n * V + 8.0 * n
         model, avail = host_cpu()
         cpu = {"value": sample_bytes / dt / 1e9, "unit": "GB/s", "cores": 1, "cpu_model": model,
-               "host_cores_available": avail, "kind": "oracle",
+               "host_cores_available": avail, "kind": "oracle", "extrapolated": True,
                "sample": "the first %d rows (%d loss rows) of the packed row, loss and full gradient, %.1f s; "
                          "credited the same bytes per row as the GPU" % (n, nl, dt),
                "seconds": dt}
@@ -656,7 +657,8 @@ def main():
         kid = KERNELS[name if name == "rope" else name + sfx]
         cnt = lib.attn_profile_count(kid)
         times = [a.elapsed_time(b) for a, b in zip(st[:cnt], sp[:cnt])]
-        kernel_ms[name] = {"avg_ms": float(np.mean(times)), "launches_per_step": launches[name],
+        kernel_ms[name] = {"avg_ms": float(np.mean(times)), "median_ms": float(np.median(times)),
+                           "min_ms": float(np.min(times)), "launches_per_step": launches[name],
                            "launches_timed": cnt}
         lib.attn_profile_events(kid, None, None, 0)
 
@@ -678,6 +680,8 @@ def main():
         if n in kernel_ms:
             t = kernel_ms[n]["avg_ms"] * 1e-3
             per_kernel[n] = {"ms": round(kernel_ms[n]["avg_ms"], 4),
+                             "ms_median": round(kernel_ms[n]["median_ms"], 4),
+                             "ms_min": round(kernel_ms[n]["min_ms"], 4),
                              "frac": credited[n] * 2.0 * D * H * pairs / t / 1e12 / peak,
                              "executed_frac": executed[n] * 2.0 * D * H * pairs / t / 1e12 / peak}
     dom = max((n for n in credited if n in kernel_ms),
@@ -720,7 +724,11 @@ def main():
                    "mask": mask, "kv_chunk": w.kv_chunk, "pass": "fwd+bwd" if do_bwd else "fwd",
                    "visible_pairs": pairs, "parallelism": "single GPU"},
         ("pct_of_fp32_peak" if f32 else "pct_of_bf16_peak"): 100.0 * tflops / peak,
+        # the method's forward and backward FLOPs over their kernels' average
+        # times (the RoPE pre-passes not included)
         "fwd_tflops": fwd_flops / (kernel_ms["fwd"]["avg_ms"] * 1e-3) / 1e12,
+        "bwd_tflops": (bwd_flops / ((kernel_ms["bwd_dq"]["avg_ms"] + kernel_ms["bwd_dkdv"]["avg_ms"]) * 1e-3) / 1e12
+                       if do_bwd else None),
         "kernels_ms": {n: round(v["avg_ms"], 4) for n, v in kernel_ms.items()},
         "roofline": roofline,
         "cpu_baseline": cpu,
