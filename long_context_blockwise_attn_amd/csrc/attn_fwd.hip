@@ -11,8 +11,9 @@
 // (batch, head); each wave owns 32 rows.  Each lane rotates its query row
 // (RoPE) and multiplies it by scale * log2(e) as it loads it, and the score
 // MFMAs start from -m, the row's running max, so they leave
-// scale * log2(e) * <q', k'> - m, the exponent of exp2 itself.  Tiles of 64 keys of K and V rows sit
-// in an NSTAGE-deep LDS ring filled by buffer-to-LDS loads.  Scores are
+// scale * log2(e) * <q', k'> - m, the exponent of exp2 itself (or -inf where
+// a mask hides the key).  Tiles of 64 keys of K and V rows sit in LDS rings
+// filled by buffer-to-LDS loads and are taken in halves of 32 keys.  Scores are
 // computed transposed, S^T = K Q^T, so each lane holds one query row: the row
 // max needs one exchange between lanes l and l^32, and the running rescale of
 // O is a per-lane scalar.  O^T = V^T P^T takes P^T straight from the score
@@ -20,21 +21,29 @@
 // reads (PTile::read_tr), which deliver the keys in the order the score
 // registers hold them, so no transposed copy of V is made.
 //
-// Two wave groups run one phase apart (ping-pong, below): on every SIMD one
-// wave issues the matrix phase (S^T of the next tile, O^T += V^T P^T) while
-// the other runs the vector phase (mask, max, lazy rescale, softmax).
+// Each wave interleaves its own matrix and vector work (the software
+// pipeline below): a wave's vector instructions placed between its own
+// MFMAs issue while those run, whereas one wave issuing only MFMAs beside
+// another issuing only vector work on the same SIMD overlaps poorly (a
+// measured property of this hardware, not a documented one).
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "tile.hpp"
 
 namespace bwattn {
 
-template <int D, int NW, int NSTAGE>
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
+
+template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   constexpr int BQ = kFwdBlockQ, BK = kFwdBlockK;
   static_assert(BQ == NW * 32, "32 query rows per wave");
   static_assert(BK == 64, "two 32-key halves per tile");
-  static_assert(NSTAGE >= 3, "K of tile t+1 and V of tile t are read in the same step");
   constexpr int NDC = D / 16;  // 16-wide k steps over D for S^T
   constexpr int NDG = D / 32;  // 32-row groups of O^T over D
   constexpr float kLazy = 8.f;
@@ -42,9 +51,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   // V rows (V^T read transposed).  P = 4 would make these reads conflict-free
   // but measured no faster: its two extra pad chunks per row lengthen the loads.
   using VR = PTile<BK, D / 8, 2>;
-  constexpr int SEG_OFF = KT::kBytes + VR::kBytes;  // segment ids of the tile's keys
-  constexpr int BUF = SEG_OFF + 256;
-  __shared__ __attribute__((aligned(16))) char smem[NSTAGE * BUF];
+  constexpr int NKS = 3, NVS = 3, NSS = 4;  // K, V and segment-id slots
+  constexpr int SEG_OFF = NKS * KT::kBytes + NVS * VR::kBytes;
+  __shared__ __attribute__((aligned(16))) char smem[SEG_OFF + NSS * 256];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hl = lane >> 5, l32 = lane & 31;
@@ -108,7 +117,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   walk.start();
 
   float m = kNegInf, lsum = 0.f;  // running max (log2 units) and sum
-  f32x16 negm = f32x16{};          // -m in every register (0 while m = -inf)
+  f32x16 negm = f32x16{};          // -m in every register (0 while m = -inf): the score MFMAs start from it
   f32x16 o[NDG];
 #pragma unroll
   for (int dg = 0; dg < NDG; ++dg) o[dg] = f32x16{};
@@ -119,219 +128,289 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   TileFill<BK, D / 8, NW, 2> vfill;  // V rows
   kfill.init(D * 2, tid);
   vfill.init(D * 2, tid);
-  auto load = [&](int t, char* buf) {
-    const uint32_t rbytes = (uint32_t)min(S - t * BK, BK) * D * 2;  // rows past S read zero
-    kfill.fill(kh + (int64_t)t * BK * D, rbytes, buf);
-    vfill.fill(vh + (int64_t)t * BK * D, rbytes, buf + KT::kBytes);
-    if (use_seg && w == 0) row64_to_lds(segb, t * BK, S, buf + SEG_OFF, lane);
-  };
-  // vector-memory instructions this wave issues per tile
-  const int per_tile = kfill.count() + vfill.count() + (use_seg && w == 0 ? 1 : 0);
-  // the fewest any wave issues: a compile-time wait count.  Waiting until
-  // that many are in flight completes the wave's loads of the older of two
-  // positions (a wave with more loads also waits for a few of the newer
-  // position, issued a step earlier); a wait on the exact count would need a
-  // branch table, whose scalar code cost ~3% of the forward's time.
-  constexpr int kLeastPerTile = KT::kBlocks / NW + VR::kBlocks / NW;
-
   // --- per-tile pieces -----------------------------------------------------
-  // S^T - m of the tile in `buf` (log2 units): s[kg] holds keys
-  // k0 + 32 kg + 8 (r/4) + 4 hl + r%4
-  auto scores = [&](const char* buf, f32x16 (&s)[2]) {
-    s[0] = s[1] = negm;
-    lds_mfma_pipe<2 * NDC, 3>([&](int i) { return KT::read(buf, 32 * (i & 1), i >> 1, lane); },
-                              [&](int i, bf16x8 x) { s[i & 1] = mfma32(x, qop[i >> 1], s[i & 1]); });
+  // Start values of the score MFMAs of the half (32 keys) j of tile t: key
+  // k0 + 32 j + 8 (r/4) + 4 hl + r%4 in register r starts from -m, or from
+  // -inf where the causal, segment or sequence-end mask hides the key, so
+  // that masked scores leave the MFMAs as -inf and no vector code touches
+  // them.  The decisions are wave-uniform, and a tile tests only what it
+  // needs: the position limit (diagonal, sequence end), the segment ids
+  // (document edge), or both.
+  struct MaskPlan {
+    int k0;
+    bool lim_mask, seg_mask;
   };
-  // causal / segment / sequence-end mask of tile t.  The decisions are
-  // wave-uniform, and a tile tests only what it needs: the position limit
-  // (diagonal, sequence end), the segment ids (document edge), or both.
-  auto mask = [&](int t, const char* buf, f32x16 (&s)[2]) {
-    const int k0 = t * BK;
-    bool seg_mask = false;
+  auto mask_plan = [&](int t) {
+    MaskPlan p;
+    p.k0 = t * BK;
+    p.seg_mask = false;
     if (use_seg) {
       int2 kr = tile64_range(t64b, t);
-      seg_mask = !(kr.x == kr.y && wrange.x == wrange.y && kr.x == wrange.x);
+      p.seg_mask = !(kr.x == kr.y && wrange.x == wrange.y && kr.x == wrange.x);
     }
-    const bool lim_mask = (k0 + BK > S) || (a.causal && k0 + BK - 1 > q0);
-    if (uniform(seg_mask || lim_mask)) {
-      const int* segk = (const int*)(buf + SEG_OFF);
-      const int lim = (a.causal ? min(S - 1, row) : S - 1) - k0 - 4 * hl;  // last visible key, tile-relative
-      // keys k0 + 32 kg + 8 rq + 4 hl + e in registers s[kg][4 rq + e]
-      if (!uniform(seg_mask)) {
+    p.lim_mask = (p.k0 + BK > S) || (a.causal && p.k0 + BK - 1 > q0);
+    return p;
+  };
+  auto score_init = [&](const MaskPlan& p, const char* segbuf, int j) -> f32x16 {
+    if (!uniform(p.seg_mask || p.lim_mask)) return negm;
+    const float nm = negm[0];
+    const int lim = (a.causal ? min(S - 1, row) : S - 1) - p.k0 - 4 * hl;  // last visible key, tile-relative
+    f32x16 c;
+    if (!uniform(p.seg_mask)) {
 #pragma unroll
-        for (int kg = 0; kg < 2; ++kg)
+      for (int r = 0; r < 16; ++r) c[r] = (32 * j + 8 * (r >> 2) + (r & 3) <= lim) ? nm : kNegInf;
+    } else {
+      const int* segk = (const int*)segbuf;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) s[kg][r] = (32 * kg + 8 * (r >> 2) + (r & 3) <= lim) ? s[kg][r] : kNegInf;
-      } else {
+      for (int rq = 0; rq < 4; ++rq) {
+        const int4 sk = *(const int4*)(segk + 32 * j + 8 * rq + 4 * hl);
+        const int sk_[4] = {sk.x, sk.y, sk.z, sk.w};
 #pragma unroll
-        for (int kg = 0; kg < 2; ++kg)
-#pragma unroll
-          for (int rq = 0; rq < 4; ++rq) {
-            const int jj = 32 * kg + 8 * rq + 4 * hl;
-            const int4 sk = *(const int4*)(segk + jj);
-            const int sk_[4] = {sk.x, sk.y, sk.z, sk.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const bool vis = (uniform(lim_mask) ? (32 * kg + 8 * rq + e <= lim) : true) & (sk_[e] == segq);
-              s[kg][4 * rq + e] = vis ? s[kg][4 * rq + e] : kNegInf;
-            }
-          }
+        for (int e = 0; e < 4; ++e) {
+          const bool vis = (uniform(p.lim_mask) ? (32 * j + 8 * rq + e <= lim) : true) & (sk_[e] == segq);
+          c[4 * rq + e] = vis ? nm : kNegInf;
+        }
       }
     }
+    return c;
   };
-  // Row max of a tile's scores, relative to m (to 0 while m = -inf), in four
-  // independent chains: with the other wave of the SIMD issuing MFMAs, one
-  // dependent chain of 16 steps left this wave idle between them.
-  auto tile_max = [&](const f32x16 (&s)[2]) {
-    float mc[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) mc[c] = fmaxf(s[c >> 1][8 * (c & 1)], s[c >> 1][8 * (c & 1) + 1]);
-#pragma unroll
-    for (int e = 2; e < 8; e += 2)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) mc[c] = fmaxf(fmaxf(mc[c], s[c >> 1][8 * (c & 1) + e]), s[c >> 1][8 * (c & 1) + e + 1]);
-    return pair_max(fmaxf(fmaxf(mc[0], mc[1]), fmaxf(mc[2], mc[3])));
+  // Row max of a half tile's scores, relative to m (to 0 while m = -inf), in
+  // 8 pieces over four independent chains: chain c covers registers 4c..4c+3.
+  // (IEEE maximum: the same value as fmaxf for the scores, which are never
+  // NaN, without the canonicalising max fmaxf adds for each MFMA result.)
+  auto vmax = [](float a, float b) { return __builtin_elementwise_maximum(a, b); };
+  auto max_piece = [&](int j, const f32x16& s, float (&mc)[4]) {
+    const int c = j & 3;
+    if (j < 4)
+      mc[c] = vmax(s[4 * c], s[4 * c + 1]);
+    else
+      mc[c] = vmax(vmax(mc[c], s[4 * c + 2]), s[4 * c + 3]);
+  };
+  auto max_done = [&](const float (&mc)[4]) {
+    const float x = vmax(vmax(mc[0], mc[1]), vmax(mc[2], mc[3]));
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
   };
   // Lazy online-softmax max update.  A row's running max m is raised only
   // when its new max exceeds it by more than kLazy (log2 units); otherwise
   // the stale m stays, p <= 2^kLazy, and O is not touched.  l and O share m,
   // so the normalised result is unchanged.  The decision is per row (the
   // wave only branches when some row needs it), so a row's result depends on
-  // its own visible keys alone.  A raised m moves the tile's scores by the
-  // rise and the start value of later tiles' score MFMAs with it.
-  auto rescale = [&](float mx, f32x16 (&s)[2]) {
-    const bool grow = mx > (m == kNegInf ? kNegInf : kLazy);
-    if (__ballot(grow)) {
-      const float rise = grow ? mx : 0.f;
-      const float mnew = grow ? (m == kNegInf ? mx : m + mx) : m;
-      const float alpha = fast_exp2(grow ? m - mnew : 0.f);  // 0 from m = -inf, where l and O are 0
-      lsum *= alpha;
+  // its own visible keys alone.  A raised m moves the half tile's scores by
+  // the rise and the start value of later score MFMAs with it.
+  auto grows = [&](float mx) { return mx > (m == kNegInf ? kNegInf : kLazy); };
+  // (grows: the row's vote; rescale: what the wave does when any row votes)
+  auto rescale = [&](float mx, bool grow, f32x16& s) {
+    const float rise = grow ? mx : 0.f;
+    const float mnew = grow ? (m == kNegInf ? mx : m + mx) : m;
+    const float alpha = fast_exp2(grow ? m - mnew : 0.f);  // 0 from m = -inf, where l and O are 0
+    lsum *= alpha;
 #pragma unroll
-      for (int dg = 0; dg < NDG; ++dg) o[dg] *= alpha;
+    for (int dg = 0; dg < NDG; ++dg) o[dg] *= alpha;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[0][r] -= rise;
-        s[1][r] -= rise;
-      }
-      m = mnew;
-      const float nm = (m == kNegInf) ? 0.f : -m;
+    for (int r = 0; r < 16; ++r) s[r] -= rise;
+    m = mnew;
+    const float nm = (m == kNegInf) ? 0.f : -m;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) negm[r] = nm;
-    }
+    for (int r = 0; r < 16; ++r) negm[r] = nm;
   };
-  // P = 2^(S*scale*log2e - m) as bf16 MFMA operands pk[kc] (keys 16 kc ..),
-  // and the row sum over the same bf16 values (one chain per kc)
-  auto softmax = [&](const f32x16 (&s)[2], bf16x8 (&pk)[4]) {
-    float rsc[4] = {lsum, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      float rs = rsc[kc];
-      const int r0 = 8 * (kc & 1);
-      float p[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) p[e] = fast_exp2(s[kc >> 1][r0 + e]);
-      u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                  pack_bf16x2(p[6], p[7])};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) rs = dot2_bf16(pw[e], kBf16OnePair, rs);
-      rsc[kc] = rs;
-      pk[kc] = __builtin_bit_cast(bf16x8, pw);
-    }
-    lsum = (rsc[0] + rsc[1]) + (rsc[2] + rsc[3]);
-  };
-  auto pv = [&](const char* buf, const bf16x8 (&pk)[4]) {
-    // V^T operand for keys 16 kc .. 16 kc + 15 (the keys of pk[kc]) and d 32 dg ..
-    const char* vr = buf + KT::kBytes;
-    lds_mfma_pipe<4 * NDG, 3>([&](int i) { return VR::read_tr(vr, 16 * (i / NDG), 32 * (i % NDG), lane); },
-                              [&](int i, bf16x8 x) { o[i % NDG] = mfma32(x, pk[i / NDG], o[i % NDG]); });
+  // P = 2^(S*scale*log2e - m) of a half tile as bf16 MFMA operands pk[kc]
+  // (its keys 16 kc ..) and the row sum over the same bf16 values (one chain
+  // per kc), in 8 pieces: piece j makes the pair 2 (j % 4) of pk[j / 4]
+  auto softmax_piece = [&](int j, const f32x16& s, u32x4 (&pw)[2], float (&rs)[2]) {
+    const int kc = j >> 2, e = j & 3, r = 8 * kc + 2 * e;
+    pw[kc][e] = pack_bf16x2(fast_exp2(s[r]), fast_exp2(s[r + 1]));
+    rs[kc] = dot2_bf16(pw[kc][e], kBf16OnePair, rs[kc]);
   };
 
-  // --- ping-pong pipeline -------------------------------------------------
-  // Waves 0-3 and 4-7 form two groups with one wave of each on every SIMD.
-  // Each step has a matrix phase (S^T of tile k+1, O^T += V^T P^T of tile k)
-  // and a vector phase (mask, max, rescale and softmax of tile k+1).  Group 1
-  // runs one barrier behind group 0, so on every SIMD one wave issues MFMAs
-  // while the other runs the softmax, and they swap at each barrier.
-  // Barrier G_j: group 0 runs the matrix phase of step k between G_2k and
-  // G_2k+1, group 1 between G_2k+1 and G_2k+2.  Tile position p lives in ring
-  // slot p % 4; it is read from G_2p-2 (K of p in the matrix phase of step
-  // p-1) until G_2p+2 (V of p in group 1's matrix phase of step p).  So each
-  // wave issues position k+4 right after G_2k+2 and, before G_2k+2, waits for
-  // its loads of position k+2 (only k+3 may still be in flight).
-  static_assert(NW == 8 && NSTAGE == 4, "two groups of four waves, four-slot ring");
-  const int grp = uniform(w >> 2);
-  auto slot = [&](int p) { return smem + (p & (NSTAGE - 1)) * BUF; };
-  if (walk.t >= 0) {
-    TileWalk w1 = walk;  // position k + 1
-    w1.next();
-    TileWalk ahead = w1;  // newest position issued
-    load(uniform(walk.t), slot(0));
-    int pend = 0;
-    if (w1.t >= 0) {
-      load(uniform(w1.t), slot(1));
+  // --- software pipeline --------------------------------------------------
+  // The keys of a 64-key tile are taken in two halves of 32 (half-steps).
+  // Half-step h runs O^T += V^T P^T of half h, the softmax of half h+1 and
+  // the scores of half h+2, so the matrix work of a half-step never waits on
+  // its vector work: each wave issues its own MFMAs with its vector
+  // instructions between them (two waves per SIMD run the same program).
+  // The first part pairs the PV MFMAs with the row max of half h+1; after the
+  // max update, the second pairs the score MFMAs of half h+2 (which start from
+  // the updated -m) with the exponentials of half h+1.
+  //
+  // Step k is half-steps 2k and 2k+1: it reads V of tile position k and K
+  // and the segment ids of position k+1.  LDS: K of position p in K slot
+  // p % 3, V of p in V slot p % 3, segment ids of p in segment slot p % 4.
+  // After the barrier that opens step k every wave has left step k-1, so K
+  // and the segment ids of position k+3 and V of position k+2 go out during
+  // step k, one load between two MFMAs of its first half-step (issued in a
+  // burst after the barrier, they stalled every wave at once); before the
+  // barrier of step k+1 each wave waits for its loads issued at step k-1
+  // (those of step k may stay in flight).
+  auto kslot = [&](int p) { return smem + (p % NKS) * KT::kBytes; };
+  auto vslot = [&](int p) { return smem + NKS * KT::kBytes + (p % NVS) * VR::kBytes; };
+  auto sslot = [&](int p) { return smem + SEG_OFF + (p & (NSS - 1)) * 256; };
+  // Buffer resources of tile t's K (V) rows; a position past the end of the
+  // walk (t < 0) gets an empty resource, so its loads only write zeros into
+  // a free slot and every step issues the same loads.
+  auto rows_rsrc = [&](const uint16_t* h, int t) {
+    const int tt = max(t, 0);
+    const uint32_t rbytes = t < 0 ? 0u : (uint32_t)min(S - tt * BK, BK) * D * 2;  // rows past S read zero
+    return make_rsrc(h + (int64_t)tt * BK * D, rbytes);
+  };
+  auto seg_rsrc = [&](int t) {
+    const int tt = max(t, 0);
+    return make_rsrc(segb + tt * BK, t < 0 ? 0u : (uint32_t)(S - tt * BK) * 4);
+  };
+  auto load_k = [&](int t, int p) {
+    const i32x4 rk = rows_rsrc(kh, t);
 #pragma unroll
-      for (int p = 2; p < NSTAGE; ++p) {
-        if (ahead.t >= 0) ahead.next();
-        if (ahead.t >= 0) {
-          load(uniform(ahead.t), slot(p));
-          ++pend;
+    for (int i = 0; i < decltype(kfill)::kPer; ++i) kfill.fill_part(i, rk, kslot(p));
+    if (use_seg && w == 0) dma_b32(seg_rsrc(t), sslot(p), lane * 4);
+  };
+  auto load_v = [&](int t, int p) {
+    const i32x4 rv = rows_rsrc(vh, t);
+#pragma unroll
+    for (int i = 0; i < decltype(vfill)::kPer; ++i) vfill.fill_part(i, rv, vslot(p));
+  };
+  // the fewest K (V) loads any wave issues per tile: compile-time wait counts
+  // (a wave with more also waits for a few of the newer tile)
+  constexpr int kLeastK = KT::kBlocks / NW, kLeastV = VR::kBlocks / NW;
+  static_assert(decltype(kfill)::kPer <= 3 && decltype(vfill)::kPer <= 3, "three load slots per part");
+
+  // One half-step.  J: the half of the tile whose V rows PV reads (the
+  // scores it makes are of the same half of the next tile).  PV: o += V^T pk
+  // from V slot vb.  SM: softmax of s1 into pk.  SC: scores from the K rows
+  // in kb into s2, started by score_init.  The vector work of each part is
+  // cut into 16 slots spread evenly over its MFMAs: the row max takes the
+  // first half of the PV part's slots, its reduction and the wave's rescale
+  // vote two more, so the vote is in by the end of the PV MFMAs; exA(slot)
+  // and exB(slot) may fill the free slots of the two parts (the loads of
+  // later tiles).
+  auto half = [&](auto j_, auto pv_, auto sm_, auto sc_, const char* vb, const char* kb, const char* sb,
+                  const MaskPlan& plan, f32x16& s1, f32x16& s2, bf16x8 (&pk)[2], auto&& exA, auto&& exB) {
+    constexpr int J = decltype(j_)::value;
+    constexpr bool PV = decltype(pv_)::value, SM = decltype(sm_)::value, SC = decltype(sc_)::value;
+    float mc[4], mx = 0.f;
+    bool grow = false;
+    uint64_t vote = 0;
+    auto slotA = [&](int j) {
+      if constexpr (SM) {
+        if (j < 8) max_piece(j, s1, mc);
+        if (j == 8) mx = max_done(mc);
+        if (j == 10) {
+          grow = grows(mx);
+          vote = __ballot(grow);
         }
       }
-    }
-    int ahead_pos = 1 + pend;  // position of `ahead` when it is valid
-    wait_vmem_le(pend * per_tile);
-    __syncthreads();  // G_0
-
-    bf16x8 pk[4];
-    {
-      f32x16 s0[2];
-      scores(slot(0), s0);
-      mask(uniform(walk.t), slot(0), s0);
-      rescale(tile_max(s0), s0);
-      softmax(s0, pk);
-    }
-    if (grp == 1) __syncthreads();  // G_1: group 1 starts one phase later
-
-    // wait for position k+2 (k+3 may be in flight), barrier, issue k+4
-    auto refill = [&](int k) {
-      if (ahead.t >= 0 && ahead_pos >= k + 3)
-        wait_vmem_le<kLeastPerTile>();
-      else
-        wait_vmem_le<0>();
-      __syncthreads();
-      if (ahead.t >= 0) ahead.next();
-      if (ahead.t >= 0) {
-        ++ahead_pos;
-        load(uniform(ahead.t), slot(ahead_pos));
-      }
+      exA(j);
     };
-
-    int k = 0;
-    while (walk.t >= 0) {
-      const bool more = w1.t >= 0;
-      f32x16 s_next[2];
-      __builtin_amdgcn_s_setprio(1);
-      if (more) scores(slot(k + 1), s_next);
-      pv(slot(k), pk);
-      __builtin_amdgcn_s_setprio(0);
-      if (grp == 0)
-        __syncthreads();
-      else
-        refill(k);
-      if (more) {
-        mask(uniform(w1.t), slot(k + 1), s_next);
-        rescale(tile_max(s_next), s_next);
-        softmax(s_next, pk);
+    if constexpr (PV) {
+      lds_mfma_pipe_mixed<2 * NDG, 2, 16>(
+          [&](int i) { return VR::read_tr(vb, 32 * J + 16 * (i / NDG), 32 * (i % NDG), lane); },
+          [&](int i, bf16x8 x) { o[i % NDG] = mfma32(x, pk[i / NDG], o[i % NDG]); }, slotA);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) slotA(j);
+    }
+    if constexpr (SM) {
+      if (vote) rescale(mx, grow, s1);
+    }
+    u32x4 pw[2];
+    float rs[2] = {lsum, 0.f};
+    auto slotB = [&](int j) {
+      if constexpr (SM) {
+        if ((j & 1) == 0) softmax_piece(j >> 1, s1, pw, rs);
       }
-      if (grp == 0)
-        refill(k);
-      else
-        __syncthreads();
-      walk = w1;
-      if (w1.t >= 0) w1.next();
+      exB(j);
+    };
+    if constexpr (SC) {
+      s2 = score_init(plan, sb, J);
+      lds_mfma_pipe_mixed<NDC, 3, 16>([&](int i) { return KT::read(kb, 32 * J, i, lane); },
+                                      [&](int i, bf16x8 x) { s2 = mfma32(x, qop[i], s2); }, slotB);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) slotB(j);
+    }
+    if constexpr (SM) {
+      lsum = rs[0] + rs[1];
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) pk[kc] = __builtin_bit_cast(bf16x8, pw[kc]);
+    }
+  };
+  auto nop = [](int) {};
+  using T_ = BoolC<true>;
+  using F_ = BoolC<false>;
+  using J0 = std::integral_constant<int, 0>;
+  using J1 = std::integral_constant<int, 1>;
+
+  if (walk.t >= 0) {
+    // tile indices of positions k+1, k+2 (-1 past the end) as step k starts;
+    // `lw` walks the newest K position issued
+    TileWalk lw = walk;
+    const int t0 = walk.t;
+    int t1, t2;
+    load_k(t0, 0);
+    lw.next();
+    t1 = lw.t;
+    load_k(t1, 1);
+    load_v(t0, 0);
+    wait_vmem_le<kLeastK + kLeastV>();
+    __syncthreads();  // step -1: K of position 0 is in
+    if (lw.t >= 0) lw.next();
+    t2 = lw.t;
+    load_k(t2, 2);
+    load_v(t1, 1);
+    bf16x8 pk[2];
+    f32x16 sA, sB;
+    {
+      const MaskPlan p0 = mask_plan(t0);
+      half(J0{}, F_{}, F_{}, T_{}, nullptr, kslot(0), sslot(0), p0, sB, sA, pk, nop, nop);  // scores of (0, 0)
+      half(J1{}, F_{}, T_{}, T_{}, nullptr, kslot(0), sslot(0), p0, sA, sB, pk, nop,
+           nop);  // softmax (0, 0), scores (0, 1)
+    }
+    // step k: s of (k, 1) in sB.  Every step issued the same loads (empty
+    // ones past the end of the walk), so a constant wait count holds.
+    int k = 0;
+    auto sync = [&]() {
+      wait_vmem_le<kLeastK + kLeastV>();
+      __syncthreads();
+      if (lw.t >= 0) lw.next();
+      return (int)lw.t;
+    };
+    while (t1 >= 0) {
+      const int t3 = sync();
+      const MaskPlan p1 = mask_plan(t1);
+      const char* vb = vslot(k);
+      const char* kb = kslot(k + 1);
+      const char* sb = sslot(k + 1);
+      // loads of K of position k+3 (and its segment ids) and V of k+2, one
+      // between MFMAs, into slots that step k-1 was the last to read
+      const i32x4 rk = rows_rsrc(kh, t3), rv = rows_rsrc(vh, t2), rsg = seg_rsrc(t3);
+      char* kd = kslot(k + 3);
+      char* vd = vslot(k + 2);
+      char* sd = sslot(k + 3);
+      auto exA = [&](int j) {
+        if (j == 11) kfill.fill_part(0, rk, kd);
+        if constexpr (decltype(kfill)::kPer > 1)
+          if (j == 13) kfill.fill_part(1, rk, kd);
+        if constexpr (decltype(kfill)::kPer > 2)
+          if (j == 15) kfill.fill_part(2, rk, kd);
+      };
+      auto exB = [&](int j) {
+        if (j == 1) vfill.fill_part(0, rv, vd);
+        if constexpr (decltype(vfill)::kPer > 1)
+          if (j == 3) vfill.fill_part(1, rv, vd);
+        if constexpr (decltype(vfill)::kPer > 2)
+          if (j == 5) vfill.fill_part(2, rv, vd);
+        if (j == 7 && use_seg && w == 0) dma_b32(rsg, sd, lane * 4);
+      };
+      half(J0{}, T_{}, T_{}, T_{}, vb, kb, sb, p1, sB, sA, pk, exA, exB);  // PV (k, 0), softmax (k, 1), scores (k+1, 0)
+      half(J1{}, T_{}, T_{}, T_{}, vb, kb, sb, p1, sA, sB, pk, nop, nop);  // PV (k, 1), softmax (k+1, 0), scores (k+1, 1)
+      t1 = t2;
+      t2 = t3;
       ++k;
     }
-    if (grp == 0) __syncthreads();  // matches group 1's extra barrier
+    sync();
+    const MaskPlan none{};
+    const char* vb = vslot(k);
+    half(J0{}, T_{}, T_{}, F_{}, vb, nullptr, nullptr, none, sB, sA, pk, nop, nop);  // PV (k, 0), softmax (k, 1)
+    half(J1{}, T_{}, F_{}, F_{}, vb, nullptr, nullptr, none, sA, sB, pk, nop, nop);  // PV (k, 1)
   }
 
   // epilogue: O = O^T / l, LSE = ln2 (m + log2 l)
@@ -353,12 +432,12 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
 }
 
 hipError_t launch_attn_fwd(const FwdArgs& a, int D, hipStream_t st) {
-  constexpr int NW = 8, NSTAGE = 4;
+  constexpr int NW = 8;
   dim3 grid((unsigned)((int64_t)a.B * a.H * a.n_qtiles)), block(NW * 64);
   if (D == 128)
-    hipLaunchKernelGGL((attn_fwd_kernel<128, NW, NSTAGE>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<128, NW>), grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<64, NW, NSTAGE>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<64, NW>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 

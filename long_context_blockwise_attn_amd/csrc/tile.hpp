@@ -126,10 +126,12 @@ struct TileFill {
   __device__ void fill(const void* src, uint32_t bytes, char* tile) const {
     const i32x4 rs = make_rsrc(src, bytes);
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      int blk = w + NW * i;
-      if (kBlocks % NW == 0 || blk < kBlocks) dma_b128(rs, tile + blk * 1024, voff[i]);
-    }
+    for (int i = 0; i < kPer; ++i) fill_part(i, rs, tile);
+  }
+  // the i-th of this wave's loads of a fill (i < kPer) from resource rs
+  __device__ void fill_part(int i, i32x4 rs, char* tile) const {
+    const int blk = w + NW * i;
+    if (kBlocks % NW == 0 || blk < kBlocks) dma_b128(rs, tile + blk * 1024, voff[i]);
   }
 };
 
@@ -194,6 +196,24 @@ __device__ __forceinline__ void lds_mfma_pipe(Rd&& rd, Mm&& mm) {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// lds_mfma_pipe with M vector-ALU pieces vc(0..M-1) spread evenly between
+// the N MFMAs: the pieces of a step issue while its MFMA runs.
+template <int N, int LA, int M, class Rd, class Mm, class Vc>
+__device__ __forceinline__ void lds_mfma_pipe_mixed(Rd&& rd, Mm&& mm, Vc&& vc) {
+  decltype(rd(0)) r[N];
+#pragma unroll
+  for (int i = 0; i < LA && i < N; ++i) r[i] = rd(i);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (i + LA < N) r[i + LA] = rd(i + LA);
+    mm(i, r[i]);
+#pragma unroll
+    for (int j = i * M / N; j < (i + 1) * M / N; ++j) vc(j);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Max and sum over the two lanes l and l ^ 32 (v_permlane32_swap).
 __device__ __forceinline__ float pair_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -207,24 +227,45 @@ __device__ __forceinline__ float pair_sum(float x) {
 __device__ __forceinline__ int2 range_union(int2 a, int2 b) { return make_int2(min(a.x, b.x), max(a.y, b.y)); }
 __device__ __forceinline__ bool ranges_meet(int2 a, int2 b) { return !(a.y < b.x || a.x > b.y); }
 
-// Segment-id range of rows [r0, r0 + rows) from the 32-row block ranges.
+// Loads from a table this kernel only reads, at a wave-uniform address,
+// through the scalar cache, waiting for the result in the same asm block.
+// The compiler makes plain loads from these tables vector loads (the
+// buffer-to-LDS asm may write memory, as far as it knows), and the zero
+// vector-memory count it then waits for would also wait for every
+// buffer-to-LDS load in flight.  Call them where no LDS read is in flight
+// that the wait would stall on.
+__device__ __forceinline__ int2 scalar_load(const int2* p) {
+  const uint64_t a = ((uint64_t)(uint32_t)uniform((int)(uint32_t)(uintptr_t)p)) |
+                     ((uint64_t)(uint32_t)uniform((int)(uint32_t)((uintptr_t)p >> 32)) << 32);
+  uint64_t v;
+  asm volatile("s_load_dwordx2 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(a));
+  return make_int2((int)(uint32_t)v, (int)(uint32_t)(v >> 32));
+}
+__device__ __forceinline__ int4 scalar_load(const int4* p) {
+  const uint64_t a = ((uint64_t)(uint32_t)uniform((int)(uint32_t)(uintptr_t)p)) |
+                     ((uint64_t)(uint32_t)uniform((int)(uint32_t)((uintptr_t)p >> 32)) << 32);
+  i32x4 v;
+  asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(a));
+  return make_int4(v[0], v[1], v[2], v[3]);
+}
 
+// Segment-id range of rows [r0, r0 + rows) from the 32-row block ranges.
 // (r0 and rows are uniform across the wave; the loads are scalar.)
 __device__ __forceinline__ int2 seg_range(const int2* blk, int nblk, int r0, int rows) {
   r0 = uniform(r0);
   rows = uniform(rows);
   int b0 = r0 >> 5, b1 = min(nblk, (r0 + rows + 31) >> 5);
-  int2 acc = blk[b0];
-  for (int k = b0 + 1; k < b1; ++k) acc = range_union(acc, blk[k]);
+  int2 acc = scalar_load(blk + b0);
+  for (int k = b0 + 1; k < b1; ++k) acc = range_union(acc, scalar_load(blk + k));
   return acc;
 }
 
 // Segment range of 64-row tile t, and of 128-row tile t (64-row tiles 2t and
 // 2t + 1, one 16-byte scalar load), from a row of the per-64-row table (its
 // padding entries make the pair read safe at the last tile).
-__device__ __forceinline__ int2 tile64_range(const int2* t64b, int t) { return t64b[uniform(t)]; }
+__device__ __forceinline__ int2 tile64_range(const int2* t64b, int t) { return scalar_load(t64b + uniform(t)); }
 __device__ __forceinline__ int2 tile128_range(const int2* t64b, int t) {
-  const int4 v = *(const int4*)(t64b + 2 * uniform(t));
+  const int4 v = scalar_load((const int4*)(t64b + 2 * uniform(t)));
   return make_int2(min(v.x, v.z), max(v.y, v.w));
 }
 
@@ -240,6 +281,7 @@ struct TileWalk {
   int lo, hi, ct, nc, r, dir;
   int desc;  // natural order (ct == 0) only, nonzero: visit hi-1 down to lo
   int step, t;
+  int run_hi;  // ascending walks: the tiles t+1 .. run_hi-1 that are useful follow t in order (0 once ended)
   const int2* blk;
   int nblk, rows;
   int2 own;
@@ -247,9 +289,11 @@ struct TileWalk {
     return blk == nullptr || ranges_meet(seg_range(blk, nblk, tile * rows, rows), own);
   }
   __device__ void seek(int after) {
+    run_hi = desc ? 0 : hi;
     if (ct == 0 && blk == nullptr) {  // natural order, every tile useful
       int c = desc ? after - 1 : after + 1;
       t = (c >= lo && c < hi) ? c : -1;
+      if (t < 0) run_hi = 0;
       return;
     }
     if (ct == 0) {
@@ -261,6 +305,7 @@ struct TileWalk {
           if (useful(c)) { t = c; return; }
       }
       t = -1;
+      run_hi = 0;
       return;
     }
     while (step < nc) {
@@ -268,18 +313,27 @@ struct TileWalk {
       if (c < 0) c += nc;
       if (c >= nc) c -= nc;
       int c1 = min(hi, (c + 1) * ct);
+      run_hi = c1;
       for (int x = max(max(lo, c * ct), after + 1); x < c1; ++x)
         if (useful(x)) { t = x; return; }
       ++step;
       after = -1;
     }
     t = -1;
+    run_hi = 0;
   }
   __device__ void start() {
     step = 0;
     seek(ct == 0 && desc ? hi : lo - 1);
   }
-  __device__ void next() { seek(t); }
+  // the common case (the next tile of the same run) without the search
+  __device__ void next() {
+    if (t + 1 < run_hi && useful(t + 1)) {
+      ++t;
+      return;
+    }
+    seek(t);
+  }
 };
 
 // Set a walk's range from a range-table entry: the per-tile segment test
