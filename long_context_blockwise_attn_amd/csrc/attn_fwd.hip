@@ -51,7 +51,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   // V rows (V^T read transposed).  P = 4 would make these reads conflict-free
   // but measured no faster: its two extra pad chunks per row lengthen the loads.
   using VR = PTile<BK, D / 8, 2>;
-  constexpr int NKS = 3, NVS = 3, NSS = 4;  // K, V and segment-id slots
+  constexpr int NKS = 4, NVS = 4, NSS = 4;  // K, V and segment-id slots
   constexpr int SEG_OFF = NKS * KT::kBytes + NVS * VR::kBytes;
   __shared__ __attribute__((aligned(16))) char smem[SEG_OFF + NSS * 256];
 
@@ -234,14 +234,16 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   // the updated -m) with the exponentials of half h+1.
   //
   // Step k is half-steps 2k and 2k+1: it reads V of tile position k and K
-  // and the segment ids of position k+1.  LDS: K of position p in K slot
-  // p % 3, V of p in V slot p % 3, segment ids of p in segment slot p % 4.
-  // After the barrier that opens step k every wave has left step k-1, so K
-  // and the segment ids of position k+3 and V of position k+2 go out during
-  // step k, one load between two MFMAs of its first half-step (issued in a
-  // burst after the barrier, they stalled every wave at once); before the
-  // barrier of step k+1 each wave waits for its loads issued at step k-1
-  // (those of step k may stay in flight).
+  // and the segment ids of position k+1.  LDS: K, V and segment ids of
+  // position p in slot p % 4 of their rings.  Step k issues K and the
+  // segment ids of position k+3 and V of position k+2, one load between two
+  // MFMAs of its first half-step (issued in a burst after a barrier, they
+  // stalled every wave at once).  Only even steps open with a barrier, after
+  // each wave has waited for all its loads: those of step k-1 are read from
+  // step k+1 on, and no wave can still be in step k-1 when one issues into
+  // the slots that steps k-2 and earlier read.  With four slots per ring a
+  // load never lands in a slot some wave may still read, and half of the
+  // barriers go.
   auto kslot = [&](int p) { return smem + (p % NKS) * KT::kBytes; };
   auto vslot = [&](int p) { return smem + NKS * KT::kBytes + (p % NVS) * VR::kBytes; };
   auto sslot = [&](int p) { return smem + SEG_OFF + (p & (NSS - 1)) * 256; };
@@ -368,8 +370,10 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
     // ones past the end of the walk), so a constant wait count holds.
     int k = 0;
     auto sync = [&]() {
-      wait_vmem_le<kLeastK + kLeastV>();
-      __syncthreads();
+      if ((k & 1) == 0) {
+        wait_vmem_le<0>();
+        __syncthreads();
+      }
       if (lw.t >= 0) lw.next();
       return (int)lw.t;
     };
@@ -406,7 +410,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
       t2 = t3;
       ++k;
     }
-    sync();
+    wait_vmem_le<0>();
+    __syncthreads();
     const MaskPlan none{};
     const char* vb = vslot(k);
     half(J0{}, T_{}, T_{}, F_{}, vb, nullptr, nullptr, none, sB, sA, pk, nop, nop);  // PV (k, 0), softmax (k, 1)
