@@ -117,7 +117,12 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
   walk.start();
 
   float m = kNegInf, lsum = 0.f;  // running max (log2 units) and sum
-  f32x16 negm = f32x16{};          // -m in every register (0 while m = -inf): the score MFMAs start from it
+  // -m in every register (0 while m = -inf): the score MFMAs start from it.
+  // Hidden from the optimizer (an empty asm statement) wherever it is set:
+  // knowing the 16 values equal, it kept one register and rebuilt the tile
+  // with 16 moves before every score chain.
+  f32x16 negm = f32x16{};
+  asm volatile("" : "+v"(negm));
   f32x16 o[NDG];
 #pragma unroll
   for (int dg = 0; dg < NDG; ++dg) o[dg] = f32x16{};
@@ -213,6 +218,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
     const float nm = (m == kNegInf) ? 0.f : -m;
 #pragma unroll
     for (int r = 0; r < 16; ++r) negm[r] = nm;
+    asm volatile("" : "+v"(negm));
   };
   // P = 2^(S*scale*log2e - m) of a half tile as bf16 MFMA operands pk[kc]
   // (its keys 16 kc ..) and the row sum over the same bf16 values (one chain
