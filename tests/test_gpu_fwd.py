@@ -49,6 +49,8 @@ def run_case(oracle, torch, B, H, S, D, seed, n_docs=0, causal=True, theta=1e6, 
     (1, 2, 1, 128, 0, True, 1e6, 0),         # a single token
     (1, 2, 63, 128, 0, True, 1e6, 0),
     (1, 2, 65, 64, 0, True, 1e6, 0),
+    (1, 2, 150, 128, 0, True, 1e6, 0),       # three key tiles: an odd count through the two-step barrier
+    (1, 2, 200, 64, 2, False, 1e6, 0),       # four key tiles, D = 64
     (1, 2, 257, 128, 3, True, 1e6, 0),
     (1, 2, 1024, 128, 0, True, 5e7, 256),    # ring order over 4 chunks
     (1, 2, 1024, 128, 6, False, 1e7, 128),   # ring order, non-causal, packed
